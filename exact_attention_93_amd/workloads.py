@@ -1,0 +1,103 @@
+"""Seeded synthetic workloads shared by the tests, the smoke check and the bench.
+
+This module draws inputs and picks sample rows; it holds no attention
+arithmetic.  Both the GPU path and the CPU oracle consume what it produces,
+so the two always see bit-identical input values.
+
+Recipe (one CPU generator per workload, seeded with ``seed``): q, k, v are
+drawn in that order with ``torch.randn`` in float32, q is multiplied by
+``q_std`` (4.0 for the peaked long-context case), and the result is rounded
+to bf16 (round to nearest even) unless the workload is fp32.  Layout is
+[B, N, H, d] contiguous for every tensor.
+"""
+from __future__ import annotations
+
+import math
+import random
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    dtype: str          # "fp32" or "bf16"
+    causal: bool
+    q_std: float
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def flops(self) -> float:
+        """4*B*Hq*N^2*d, halved when causal (the conventional count)."""
+        f = 4.0 * self.B * self.Hq * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    @property
+    def io_bytes(self) -> int:
+        """Bytes the forward must move at least once: q, k, v read, o and lse written."""
+        s = 4 if self.dtype == "fp32" else 2
+        return (2 * self.Hq + 2 * self.Hkv) * self.B * self.N * self.d * s + 4 * self.B * self.Hq * self.N
+
+
+# The five workloads: a tiny fp32 single head, bf16 MHA at d=64, the headline
+# causal d=128 case, a long-context case with peaked logits, and causal GQA.
+WORKLOADS = {
+    "single_head_fp32_N256_d64": Workload("single_head_fp32_N256_d64", 1, 1, 1, 256, 64, "fp32", False, 1.0, 1001),
+    "mha_bf16_B4_H16_N2048_d64": Workload("mha_bf16_B4_H16_N2048_d64", 4, 16, 16, 2048, 64, "bf16", False, 1.0, 1002),
+    "causal_bf16_B2_H32_N4096_d128": Workload("causal_bf16_B2_H32_N4096_d128", 2, 32, 32, 4096, 128, "bf16", True, 1.0, 1003),
+    "causal_bf16_B1_H32_N16384_d128_qstd4": Workload("causal_bf16_B1_H32_N16384_d128_qstd4", 1, 32, 32, 16384, 128, "bf16", True, 4.0, 1004),
+    "gqa_causal_bf16_B1_Hq32_Hkv8_N32768_d128": Workload("gqa_causal_bf16_B1_Hq32_Hkv8_N32768_d128", 1, 32, 8, 32768, 128, "bf16", True, 1.0, 1005),
+}
+ORDER = list(WORKLOADS)
+HEADLINE = "causal_bf16_B2_H32_N4096_d128"
+
+
+def make(B, Hq, Hkv, N, d, dtype="bf16", causal=False, q_std=1.0, seed=0, name="custom") -> Workload:
+    return Workload(name, B, Hq, Hkv, N, d, dtype, causal, q_std, seed)
+
+
+def gen_inputs(w: Workload):
+    """(q, k, v) on the host, drawn as described in the module docstring."""
+    g = torch.Generator(device="cpu").manual_seed(w.seed)
+    q = torch.randn((w.B, w.N, w.Hq, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((w.B, w.N, w.Hkv, w.d), generator=g, dtype=torch.float32)
+    v = torch.randn((w.B, w.N, w.Hkv, w.d), generator=g, dtype=torch.float32)
+    if w.q_std != 1.0:
+        q = q * w.q_std
+    if w.dtype == "bf16":
+        q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
+    elif w.dtype != "fp32":
+        raise ValueError(w.dtype)
+    return q.contiguous(), k.contiguous(), v.contiguous()
+
+
+def sample_rows(w: Workload, per_head: int = 512, seed: int | None = None):
+    """Query rows to check, as (b, h, i) triples.
+
+    Per (b, h): rows 0, 1, 2, 3, N-2, N-1, then uniform draws without
+    replacement until ``per_head`` rows (all rows when N <= per_head), from
+    ``random.Random(seed * 1_000_003 + b * Hq + h)``.
+    """
+    seed = w.seed if seed is None else seed
+    out = []
+    for b in range(w.B):
+        for h in range(w.Hq):
+            if w.N <= per_head:
+                rows = list(range(w.N))
+            else:
+                fixed = [0, 1, 2, 3, w.N - 2, w.N - 1]
+                rng = random.Random(seed * 1_000_003 + b * w.Hq + h)
+                rest = [i for i in rng.sample(range(4, w.N - 2), per_head - len(fixed))]
+                rows = sorted(set(fixed + rest))
+            out.extend((b, h, i) for i in rows)
+    return out

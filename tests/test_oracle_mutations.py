@@ -1,0 +1,57 @@
+"""Each plausible mistake planted in a copy of the oracle must fail a pin.
+
+The copy of oracle/ref.c is edited textually, compiled with gcc into a
+temporary directory and run through the same pins as the real oracle
+(tests/pins.py).  The real oracle is never modified.
+"""
+import functools
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ref.c")
+
+# (name, original text, planted text)
+MUTATIONS = [
+    ("dropped_scale", "s[j] = J->scale * acc;", "s[j] = acc;"),
+    ("wrong_gqa_index", "const int hk = h / g;", "const int hk = h % J->Hkv;"),
+    ("causal_off_by_one", "J->causal ? i + 1 : J->N", "J->causal ? (i > 0 ? i : 1) : J->N"),
+    ("lse_dropped_max", "*lse_out = m + log(l);", "*lse_out = log(l);"),
+    ("exp_sign", "l += exp(s[j] - m);", "l += exp(m - s[j]);"),
+    ("v_for_k", "const float *kj = J->k +", "const float *kj = J->v +"),
+    ("v_reversed_coord", "o_out[x] += a * (double)vj[x];", "o_out[x] += a * (double)vj[d - 1 - x];"),
+    ("q_from_key_row", "const float *qi = J->q + (((int64_t)b * J->N + i)", "const float *qi = J->q + (((int64_t)b * J->N + 0)"),
+    ("no_normalise", "const double a = exp(s[j] - m) / l;", "const double a = exp(s[j] - m);"),
+    ("max_not_subtracted_in_weights", "const double a = exp(s[j] - m) / l;", "const double a = exp(s[j]) / l;"),
+]
+
+
+@functools.lru_cache(maxsize=None)
+def _build(name, tmpdir):
+    src = open(SRC).read()
+    orig, new = next((o, n) for nm, o, n in MUTATIONS if nm == name)
+    assert src.count(orig) == 1, f"mutation site for {name} not found exactly once"
+    path = os.path.join(tmpdir, f"ref_{name}.c")
+    with open(path, "w") as f:
+        f.write(src.replace(orig, new))
+    so = os.path.join(tmpdir, f"lib_{name}.so")
+    subprocess.run(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", so, path, "-lm", "-lpthread"], check=True)
+    return so
+
+
+@pytest.mark.parametrize("name", [m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(name, tmp_path_factory):
+    so = _build(name, str(tmp_path_factory.mktemp("mut")))
+    lib = oracle._open(so)
+    att = functools.partial(oracle.attention, _lib_override=lib)
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(att)
+        except (AssertionError, RuntimeError, FloatingPointError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake {name}"
