@@ -1,0 +1,179 @@
+// Fused exact attention forward with fp32 inputs, output and arithmetic, on
+// the CDNA4 fp32 matrix-core instruction v_mfma_f32_32x32x2_f32.
+//
+// Same algorithm and work partition as the bf16 kernel (Q-block-outer loop,
+// online-softmax merge with deferred normalisation, causal tiles above the
+// diagonal skipped; see fa_fwd_bf16.hip for the citations), written for
+// accuracy rather than peak speed: 32-key tiles, one LDS buffer, V kept in
+// its natural [key][d] layout.
+//
+// Layout (32x32x2 fp32 MFMA): A lane l supplies A[l % 32][l / 32], B lane l
+// supplies B[l / 32][l % 32]; the 32x32 accumulator holds column l % 32 in
+// lane l and row 8*(i/4) + 4*(l/32) + (i%4) in register i.  S^T = K Q^T puts
+// query l % 32 in lane l; O^T = V^T P^T then takes P^T straight from the
+// S^T registers, one key pair (register i of both lane halves) per step.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kBM = kBlockM;
+constexpr int kBN = 32;
+constexpr int kThreads = 256;
+constexpr float kLn2 = 0.693147180559945309f;
+
+__device__ __forceinline__ f32x16_t mfma_f32(float a, float b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kThreads) fwd_f32_kernel(FwdParams p)
+{
+    constexpr int KP = D + 4;              // K row pitch (floats)
+    constexpr int S4 = D / 8;              // float4 groups of Q per lane
+    constexpr int XB = D / 32;
+    constexpr int LOADS = kBN * D / 4 / kThreads;   // float4 loads per thread per tensor
+
+    __shared__ __attribute__((aligned(16))) float Ks[kBN * KP];
+    __shared__ __attribute__((aligned(16))) float Vs[kBN * D];
+
+    int b, h, tile;
+    decode_tile(p, b, h, tile);
+    const int hk = h / p.group;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int lq = lane & 31, hf = lane >> 5;
+    const int N = p.N;
+    const int q_first = tile * kBM;
+    const int wq0 = q_first + wave * 32;
+    const int my_q = wq0 + lq;
+    const float c = p.c;
+
+    const int sQ = p.Hq * D, sK = p.Hkv * D;
+    const float *qbase = (const float *)p.q + ((int64_t)b * N * p.Hq + h) * D;
+    const float *kbase = (const float *)p.k + ((int64_t)b * N * p.Hkv + hk) * D;
+    const float *vbase = (const float *)p.v + ((int64_t)b * N * p.Hkv + hk) * D;
+
+    // Q^T operand: step (s, e) of the contraction uses d = 8s + 4hf + e.
+    f32x4_t qreg[S4];
+    const float qmul = p.qmode == 1 ? -1.f : 1.f;
+#pragma unroll
+    for (int s = 0; s < S4; ++s) {
+        if (my_q < N && p.qmode != 2) qreg[s] = *(const f32x4_t *)(qbase + my_q * sQ + 8 * s + 4 * hf) * qmul;
+        else qreg[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+
+    int nkt = (N + kBN - 1) / kBN;
+    if (CAUSAL) nkt = (min(q_first + kBM, N) - 1) / kBN + 1;
+
+    float m_run = -INFINITY, l_run = 0.f;
+    f32x16_t oacc[XB];
+#pragma unroll
+    for (int xb = 0; xb < XB; ++xb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[xb][i] = 0.f;
+
+    for (int j = 0; j < nkt; ++j) {
+        const int key0 = j * kBN;
+        __syncthreads();   // previous tile fully consumed
+#pragma unroll
+        for (int r = 0; r < LOADS; ++r) {
+            const int idx = tid + r * kThreads;          // float4 index within the tile
+            const int row = idx / (D / 4), col = (idx % (D / 4)) * 4;
+            const int key = key0 + row;
+            f32x4_t kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+            if (key < N) {
+                kv = *(const f32x4_t *)(kbase + key * sK + col);
+                vv = *(const f32x4_t *)(vbase + key * sK + col);
+            }
+            *(f32x4_t *)&Ks[row * KP + col] = kv;
+            *(f32x4_t *)&Vs[row * D + col] = vv;
+        }
+        __syncthreads();
+        if (CAUSAL && key0 > wq0 + 31) continue;   // whole tile above this wave's rows
+
+        f32x16_t sacc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+#pragma unroll
+        for (int s = 0; s < S4; ++s) {
+            const f32x4_t a = *(const f32x4_t *)&Ks[lq * KP + 8 * s + 4 * hf];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sacc = mfma_f32(a[e], qreg[s][e], sacc);
+        }
+        if ((key0 + kBN > N) || (CAUSAL && key0 + kBN - 1 > wq0)) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = key0 + 8 * (i >> 2) + 4 * hf + (i & 3);
+                if (!(key < N && (!CAUSAL || key <= my_q))) sacc[i] = -INFINITY;
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx * c);
+        const float m_sub = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = exp2f(m_run - m_sub);
+        m_run = m_new;
+        float rs = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float e = exp2f(__builtin_fmaf(sacc[i], c, -m_sub));
+            sacc[i] = e;
+            rs += e;
+        }
+        l_run = l_run * alpha + rs;
+#pragma unroll
+        for (int xb = 0; xb < XB; ++xb) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[xb][i] *= alpha;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int key = 8 * (i >> 2) + 4 * hf + (i & 3);
+                oacc[xb] = mfma_f32(Vs[key * D + xb * 32 + lq], sacc[i], oacc[xb]);
+            }
+        }
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (my_q < N) {
+        const float inv = 1.f / l_tot;
+        float *orow = (float *)p.o + ((int64_t)b * N * p.Hq + h) * D + my_q * sQ;
+#pragma unroll
+        for (int xb = 0; xb < XB; ++xb)
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                const int x = xb * 32 + 8 * gi + 4 * hf;
+                f32x4_t w = {oacc[xb][4 * gi] * inv, oacc[xb][4 * gi + 1] * inv,
+                             oacc[xb][4 * gi + 2] * inv, oacc[xb][4 * gi + 3] * inv};
+                *(f32x4_t *)(orow + x) = w;
+            }
+        if (hf == 0) p.lse[((int64_t)b * p.Hq + h) * N + my_q] = m_run * kLn2 + logf(l_tot);
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_one(const FwdParams &p, hipStream_t stream)
+{
+    const unsigned grid = (unsigned)p.B * (unsigned)p.Hq * (unsigned)p.ntiles;
+    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(const FwdParams &p, int d, hipStream_t stream)
+{
+    if (d == 128) return p.causal ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
+    return p.causal ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
+}
+
+}  // namespace fa
