@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one call of fa_fwd (the whole hot path) over the headline workload:
+causal attention, B=2, H=32, N=4096, d=128, bf16 inputs and output, fp32
+accumulation, synthetic inputs already resident in HBM.  W untimed warm-up
+steps, then exactly K steps between a synchronisation on each side, timed
+with events on the stream the kernel runs on (one event before each launch,
+one after the last).  One JSON line is printed.
+
+value = conventional FLOPs (4*B*H*N^2*d, halved for causal) / mean step time.
+roofline: achieved = the same FLOPs per launch / mean launch duration, against
+the dense bf16 matrix-core peak of MI355X (2.5 PFLOP/s); traffic = HBM bytes
+per launch from the committed rocprofv3 counter summary, used only while the
+kernel sources still hash to the value recorded there (else null).
+cpu_baseline: the fp64 CPU oracle, timed on this host's cores over a bounded
+sample of the same workload's query rows, in the same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s at N=4096,d=128 causal bf16; % of dense bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak (published)
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "fa_fwd_bf16_causal_B2_H32_N4096_d128_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources and the public header."""
+    from exact_attention_93_amd import _build
+    h = hashlib.sha256()
+    for path in _build.sources() + [os.path.join(ROOT, "include", "fa.h")]:
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed counter summary, or None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, seconds: float):
+    """Time the fp64 oracle on the headline workload's sampled query rows."""
+    import numpy as np
+    import oracle
+    from exact_attention_93_amd import workloads as W
+
+    q, k, v = W.gen_inputs(w)
+    bb, hh, ii = np.meshgrid(np.arange(w.B), np.arange(w.Hq), np.arange(w.N), indexing="ij")
+    rows = np.stack([bb.ravel(), hh.ravel(), ii.ravel()], axis=1)   # every query row
+    threads = oracle.host_threads()
+    # calibrate on a small slice, then size the sample to about `seconds`
+    probe = rows[:: max(1, len(rows) // (8 * threads))][: 4 * threads]
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, w.scale, w.causal, rows=probe, threads=threads)
+    dt = max(time.perf_counter() - t0, 1e-3)
+    n = int(min(len(rows), max(len(probe), len(probe) * seconds / dt)))
+    pick = rows[np.linspace(0, len(rows) - 1, n).astype(int)]
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, w.scale, w.causal, rows=pick, threads=threads)
+    dt = time.perf_counter() - t0
+    vis = (pick[:, 2] + 1) if w.causal else np.full(len(pick), w.N)
+    flops = float(4.0 * w.d * vis.sum())
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+        "sample": (f"all {n} query rows of {w.name}" if n == len(rows) else
+                   f"{n} of the {len(rows)} query rows of {w.name}, evenly strided over (b, h, i)")
+                  + f"; fp64 3-pass oracle, {dt:.1f} s wall; FLOPs counted as 4*d per visible key",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline case)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for cpu_baseline (0: skip)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain copy of this many MiB (counter calibration runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+              "(the forward would shard by (batch, head) with no exchange)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_93_amd as fa
+    from exact_attention_93_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    fa.load_library()   # fails loudly if libfa.so is missing
+
+    w = W.WORKLOADS[args.workload or W.HEADLINE]
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in W.gen_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        torch.cuda.synchronize()
+        print(f"# calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written per neg kernel",
+              file=sys.stderr, flush=True)
+
+    def step():
+        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i].record(stream)
+        step()
+    ev[K].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(K)]       # ms per launch
+    total_ms = ev[0].elapsed_time(ev[K])
+    ms_per_step = total_ms / K
+    mean_launch_ms = sum(per) / K
+    if not (torch.isfinite(o.float()).all() and torch.isfinite(lse).all()):
+        print("bench.py: non-finite output", file=sys.stderr)
+        sys.exit(1)
+
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (mean_launch_ms * 1e-3) / 1e12
+    traffic = read_traffic()
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded randn, bf16 round-to-nearest-even)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "io_dtype": w.dtype, "accumulate": "fp32", "layout": "BNHD",
+                   "flops_per_step": w.flops, "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "timing": {"mean_launch_us": round(mean_launch_ms * 1e3, 2), "min_launch_us": round(min(per) * 1e3, 2),
+                   "max_launch_us": round(max(per) * 1e3, 2), "host_wall_s": round(wall, 4),
+                   "kernel_source_hash": kernel_source_hash()},
+    }
+    if args.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
