@@ -31,6 +31,12 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    # A kernel whose host-side stub went missing would only fail at load time.
+    und = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True, check=True).stdout
+    bad = [ln.split()[-1] for ln in und.splitlines() if "device_stub" in ln or "_ZN2fa" in ln]
+    if bad:
+        os.remove(tmp)
+        raise RuntimeError(f"libfa.so has undefined library symbols: {bad}")
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -28,9 +28,10 @@ int validate_and_fill(const void *q, const void *k, const void *v, void *o, floa
     if (B < 1 || Hq < 1 || Hkv < 1 || N < 1) return FA_ERR_SHAPE;
     if (Hq % Hkv != 0) return FA_ERR_HEADS;
     if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-    // 32-bit element offsets inside one batch entry, 32-bit grid
+    // 32-bit byte offsets inside one batch entry (also for the up to 255 rows
+    // past N that the kernels' range-checked loads may address), 32-bit grid
     const int64_t hmax = Hq > Hkv ? Hq : Hkv;
-    if ((int64_t)N * hmax * d >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+    if (((int64_t)N + 256) * hmax * d >= ((int64_t)1 << 29)) return FA_ERR_SHAPE;
     const int64_t ntiles = ((int64_t)N + fa::kBlockM - 1) / fa::kBlockM;
     if ((int64_t)B * Hq * ntiles >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGN;

@@ -18,27 +18,38 @@
 // and each owns 32 whole query rows, so row statistics never cross
 // wavefronts (the "sliced-Q" partition the pages credit to FlashAttention-2).
 //
+// Data movement: K and V tiles go from HBM straight into LDS with 16-byte
+// buffer loads (buffer_load_dwordx4 ... lds), double-buffered so that tile
+// j+1 streams in while tile j is computed.  The buffer descriptor's range
+// check returns zeros for keys past the end of the sequence, so no address
+// ever leaves the tensors.  Both tiles keep their natural [key][d] layout,
+// with the 16-byte chunks of each row permuted by an XOR of the row index so
+// that the matrix-core operand reads below hit distinct LDS banks.
+//
 // Matrix-core layout (v_mfma_f32_32x32x16_bf16, D = A*B + C, 32x32 output):
 // the kernel computes the TRANSPOSED score tile S^T = K Q^T (A = K from LDS,
 // B = Q^T from registers).  A 32x32 accumulator holds column (lane % 32) in
 // every lane, so lane l owns query (l % 32) and 16 of the 32 keys of a block;
 // the other 16 are in lane l ^ 32.  A row maximum or sum is therefore 16
-// in-lane operations plus one exchange between the two lane halves.  The K
-// rows are fed to the A operand in a permuted order (bits 2 and 3 of the row
-// index swapped) so that accumulator register i of lane half hf holds key
-// 16*(i/8) + 8*hf + (i%8): exactly the slots the B operand of the next
-// product expects.  The probabilities then feed O^T = V^T P^T straight from
-// registers (B = P^T, A = V^T from LDS), and the O^T accumulator again has
-// one query per lane, so the rescale by exp(m_old - m_new) is a per-lane
-// scalar.  V is written to LDS transposed ([d][key]) so that each A-operand
-// fetch is one 16-byte read.
+// in-lane operations plus one exchange between the two lane halves
+// (v_permlane32_swap).  The K rows are fed to the A operand in a permuted
+// order (bits 2 and 3 of the row index swapped) so that accumulator register
+// i of lane half hf holds key 16*(i/8) + 8*hf + (i%8): exactly the slots the
+// B operand of the next product expects.  The probabilities then feed
+// O^T = V^T P^T straight from registers (B = P^T), and the O^T accumulator
+// again has one query per lane, so the rescale by exp(m_old - m_new) is a
+// per-lane scalar.  The A operand V^T is read from the untransposed V tile
+// with the LDS transpose read ds_read_b64_tr_b16: within each group of 16
+// lanes, lane i receives element i%4 of the 8-byte rows addressed by lanes
+// 4e + i/4 (e = 0..3), so pointing lane 4e+q at V[k0+e][x0+4q..x0+4q+3]
+// hands lane i the four keys k0..k0+3 of column x0+i.
 //
 // Exponentials are taken base 2 with scale*log2(e) folded into one FMA per
 // score.  The accumulator is only rescaled when some row's maximum grows by
 // more than kLazyLog2 (base-2 units) over the reference value in use: the
-// result does not depend on which reference value is subtracted ("the
-// softmax identity holds for any m", second page, section 5.1), the values
-// stay bounded by 2^kLazyLog2, and the final division uses the same l.
+// result does not depend on which reference value is subtracted (the softmax
+// identity holds for any m, second page, section 5.1), the values stay
+// bounded by 2^kLazyLog2, and the final division uses the same sums.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -53,6 +64,9 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int kBM = kBlockM;   // query rows per workgroup
 constexpr int kBN = 64;        // keys per K/V tile
@@ -80,9 +94,46 @@ __device__ __forceinline__ float sum_bf16x2(uint32_t pair, float acc)
                                            __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
 }
 
-__device__ __forceinline__ float other_half(float x)
+// v_permlane32_swap exchanges the upper lane half of its first operand with
+// the lower half of its second; with x in both, the two results hold x of
+// this lane and of lane ^ 32 (in some order), so a symmetric operation on
+// them combines the two halves identically in every lane.
+__device__ __forceinline__ float max_halves(float x)
 {
-    return __shfl_xor(x, 32);
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Chunk permutations of the LDS tiles (chunk = 16 bytes; a row is D/8 chunks).
+// K: the 16 rows one phase of a 16-byte operand read touches land in 16
+// distinct bank groups.  V: the 4 rows x 4 chunks one phase of the transpose
+// read touches land in 16 distinct bank groups.
+template <int D> __device__ __forceinline__ int k_swz(int row)
+{
+    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D> __device__ __forceinline__ int v_swz(int row)
+{
+    return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
+// 16 bytes per lane from base + off (bytes) straight into LDS at dst + 16*lane,
+// through a buffer descriptor whose range check returns zeros at or past
+// `range` bytes.
+__device__ __forceinline__ void load_lds16(const void *base, int range, uint32_t off, lds_void_t *dst)
+{
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, range, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off, 0, 0, 0);
+}
+
+__device__ __forceinline__ void lds_wait_vm()
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <int D, bool CAUSAL>
@@ -92,14 +143,22 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p)
     constexpr int XB = D / 32;                     // 32-row blocks of O^T
     constexpr int NKB = kBN / 32;                  // 32-key blocks per tile
     constexpr int PVSTEPS = kBN / 16;              // K-steps of O^T = V^T P^T
-    constexpr int KCH = D / 8;                     // 16-byte chunks per row
-    constexpr int RPP = kThreads / KCH;            // rows per load pass
-    constexpr int LOADS = kBN / RPP;               // 16-byte loads per thread per tensor
-    constexpr int VT_PITCH = kBN + 8;              // V^T row pitch (elements)
-    static_assert(LOADS == 2 || LOADS == 4, "tile shape");
+    constexpr int CHUNKS = D / 8;                  // 16-byte chunks per row
+    constexpr int ROW_BYTES = D * 2;
+    constexpr int ROWS_PER_BLK = 1024 / ROW_BYTES; // rows per 1 KB direct-load block
+    constexpr int BLKS = kBN * ROW_BYTES / 1024;   // 1 KB blocks per tile and tensor
+    constexpr int BLKS_PER_WAVE = BLKS / (kThreads / 64);
+    constexpr int TILE_ELEMS = kBN * D;
+    static_assert(BLKS_PER_WAVE >= 1, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kBN * D];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VT_PITCH];
+    // Two stages of K and V as four distinct objects: the loop below names
+    // each stage statically, so the compiler can see that the loads filling
+    // one stage never alias the operand reads of the other and does not make
+    // those reads wait for the loads in flight.
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks0[TILE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks1[TILE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs0[TILE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs1[TILE_ELEMS];
 
     int b, h, tile;
     decode_tile(p, b, h, tile);
@@ -117,6 +176,9 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p)
     const uint16_t *qbase = (const uint16_t *)p.q + ((int64_t)b * N * p.Hq + h) * D;
     const uint16_t *kbase = (const uint16_t *)p.k + ((int64_t)b * N * p.Hkv + hk) * D;
     const uint16_t *vbase = (const uint16_t *)p.v + ((int64_t)b * N * p.Hkv + hk) * D;
+    // Loads cover rows 0..N-1 of this (batch, kv head): anything at or past
+    // row N reads as zero.
+    const int range = N * sK * 2;
 
     // ---- Q^T operand: lane (lq, hf) holds q[my_q][16t + 8hf .. +7] for step t
     u32x4_t qreg[KSTEPS];
@@ -144,50 +206,28 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p)
         nkt = last_q / kBN + 1;
     }
 
-    // ---- global -> register staging of one K/V tile
-    const int ch = tid % KCH;      // 16-byte chunk of a row this thread moves
-    const int rg = tid / KCH;      // row (K) / key group (V) this thread moves
-    u32x4_t kst[LOADS], vst[LOADS];
-    auto gload = [&](int j) {
-        const int key0 = j * kBN;
+    // ---- HBM -> LDS: each wavefront moves BLKS_PER_WAVE 1 KB blocks of K
+    // and of V per tile; lane l fills physical chunk l % CHUNKS of row
+    // l / CHUNKS of its block.
+    const int ld_row = lane / CHUNKS, ld_pch = lane % CHUNKS;
+    auto issue_tile = [&](int j, uint16_t *kdst, uint16_t *vdst) {
 #pragma unroll
-        for (int r = 0; r < LOADS; ++r) {
-            const int key = key0 + rg + r * RPP;
-            kst[r] = key < N ? *(const u32x4_t *)(kbase + key * sK + ch * 8) : u32x4_t{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int r = 0; r < LOADS; ++r) {
-            const int key = key0 + rg * LOADS + r;
-            vst[r] = key < N ? *(const u32x4_t *)(vbase + key * sK + ch * 8) : u32x4_t{0, 0, 0, 0};
-        }
-    };
-    // register -> LDS: K row-major with the 16-byte chunk index XOR-swizzled by
-    // the row; V transposed to [d][key].
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int r = 0; r < LOADS; ++r) {
-            const int row = rg + r * RPP;
-            *(u32x4_t *)&Ks[buf][row * D + ((ch ^ (row & (KCH - 1))) * 8)] = kst[r];
-        }
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {          // dword w holds x = 2w (low) and 2w+1 (high)
-            const int x = ch * 8 + 2 * w;
-            if constexpr (LOADS == 4) {
-                const uint32_t a0 = vst[0][w], a1 = vst[1][w], a2 = vst[2][w], a3 = vst[3][w];
-                const u32x2_t ev = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-                const u32x2_t od = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-                *(u32x2_t *)&Vt[buf][x * VT_PITCH + rg * 4] = ev;
-                *(u32x2_t *)&Vt[buf][(x + 1) * VT_PITCH + rg * 4] = od;
-            } else {
-                const uint32_t a0 = vst[0][w], a1 = vst[1][w];
-                *(uint32_t *)&Vt[buf][x * VT_PITCH + rg * 2] = (a0 & 0xffffu) | (a1 << 16);
-                *(uint32_t *)&Vt[buf][(x + 1) * VT_PITCH + rg * 2] = (a0 >> 16) | (a1 & 0xffff0000u);
-            }
+        for (int i = 0; i < BLKS_PER_WAVE; ++i) {
+            const int blk = wave * BLKS_PER_WAVE + i;
+            const int row = blk * ROWS_PER_BLK + ld_row;
+            const uint32_t rowoff = (uint32_t)(j * kBN + row) * (uint32_t)(sK * 2);
+            load_lds16(kbase, range, rowoff + ((ld_pch ^ k_swz<D>(row)) * 16), (lds_void_t *)&kdst[blk * 512]);
+            load_lds16(vbase, range, rowoff + ((ld_pch ^ v_swz<D>(row)) * 16), (lds_void_t *)&vdst[blk * 512]);
         }
     };
 
     // A-operand row for lane lq: key 32*kb + perm(lq), perm swaps bits 2 and 3.
     const int krow = (lq & 0x13) | ((lq & 4) << 1) | ((lq & 8) >> 1);
+    // Transpose-read addressing for V^T: lane group g = lane / 16, s = lane % 16.
+    const int tg = lane >> 4, ts = lane & 15;
+    const int tr_row = 8 * (tg >> 1) + (ts >> 2);            // + 16u + 4r
+    const int tr_chunk = 2 * (tg & 1) + ((ts & 3) >> 1);      // + 4xb
+    const int tr_byte = 8 * (ts & 1);
 
     float m_run = -INFINITY;   // reference maximum (base-2 units), shared by both halves
     float l_run = 0.f;         // fp32 sum of this lane half's probabilities
@@ -198,15 +238,15 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[xb][i] = 0.f;
 
-    gload(0);
-    lstore(0);
+    issue_tile(0, Ks0, Vs0);
+    lds_wait_vm();
     __syncthreads();
 
-    for (int j = 0; j < nkt; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < nkt) gload(j + 1);
-        const uint16_t *ks = Ks[buf];
-        const uint16_t *vt = Vt[buf];
+    // One K/V tile: prefetch tile j+1 into the other stage, compute tile j.
+    auto step = [&](int j, const uint16_t *ksrc, const uint16_t *vsrc, uint16_t *knext, uint16_t *vnext) {
+        if (j + 1 < nkt) issue_tile(j + 1, knext, vnext);
+        const char *ks = (const char *)ksrc;
+        const char *vs = (const char *)vsrc;
         const int key0 = j * kBN;
         const bool active = !CAUSAL || key0 <= wq0 + 31;   // some key visible to this wave
         if (active) {
@@ -217,32 +257,31 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
                 const int row = kb * 32 + krow;
-                const uint16_t *kr = ks + row * D;
+                const char *kr = ks + row * ROW_BYTES;
+                const int sw = k_swz<D>(row);
 #pragma unroll
                 for (int t = 0; t < KSTEPS; ++t) {
-                    const u32x4_t a = *(const u32x4_t *)(kr + (((2 * t + hf) ^ (row & (KCH - 1))) * 8));
+                    const u32x4_t a = *(const u32x4_t *)(kr + (((2 * t + hf) ^ sw) * 16));
                     sacc[kb] = mfma_bf16(a, qreg[t], sacc[kb]);
                 }
             }
             // ---- mask: keys past the end, and keys after the query when causal
             const bool need_mask = (key0 + kBN > N) || (CAUSAL && key0 + kBN - 1 > wq0);
             if (need_mask) {
+                const int lim = (CAUSAL ? min(my_q, N - 1) : N - 1) - (key0 + 8 * hf);
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = key0 + kb * 32 + 16 * (i >> 3) + 8 * hf + (i & 7);
-                        const bool vis = key < N && (!CAUSAL || key <= my_q);
-                        if (!vis) sacc[kb][i] = -INFINITY;
-                    }
+                    for (int i = 0; i < 16; ++i)
+                        if (kb * 32 + 16 * (i >> 3) + (i & 7) > lim) sacc[kb][i] = -INFINITY;
             }
-            // ---- row maximum of this tile (16 in-lane values per block + one exchange)
+            // ---- row maximum of this tile (in-lane, then one exchange)
             float mx = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-            mx = fmaxf(mx, other_half(mx));
+            mx = max_halves(mx);
             const float m_tile = mx * c;
             const bool grow = m_tile > m_run + kLazyLog2;
             float alpha = 1.f;
@@ -288,19 +327,32 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p)
                 rs1 = sum_bf16x2(pb[3], rs1);
 #pragma unroll
                 for (int xb = 0; xb < XB; ++xb) {
-                    const u32x4_t a = *(const u32x4_t *)(vt + (xb * 32 + lq) * VT_PITCH + 16 * u + 8 * hf);
+                    u32x4_t a;
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        const int row = 16 * u + 4 * r + tr_row;
+                        const int off = row * ROW_BYTES + (((4 * xb + tr_chunk) ^ v_swz<D>(row)) * 16) + tr_byte;
+                        const i16x4_t t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vs + off));
+                        const u32x2_t t2 = __builtin_bit_cast(u32x2_t, t4);
+                        a[2 * r] = t2[0];
+                        a[2 * r + 1] = t2[1];
+                    }
                     oacc[xb] = mfma_bf16(a, pb, oacc[xb]);
                 }
             }
             lb_run = lb_run * alpha + (rs0 + rs1);
         }
-        if (j + 1 < nkt) lstore(buf ^ 1);
+        lds_wait_vm();
         __syncthreads();
+    };
+    for (int j = 0; j < nkt; j += 2) {
+        step(j, Ks0, Vs0, Ks1, Vs1);
+        if (j + 1 < nkt) step(j + 1, Ks1, Vs1, Ks0, Vs0);
     }
 
     // ---- epilogue: O = O_acc / l (bf16, round to nearest even), lse = m ln2 + ln l
-    const float l_tot = l_run + other_half(l_run);
-    const float lb_tot = lb_run + other_half(lb_run);
+    const float l_tot = sum_halves(l_run);
+    const float lb_tot = sum_halves(lb_run);
     if (my_q < N) {
         const float inv = 1.f / lb_tot;
         uint16_t *orow = (uint16_t *)p.o + ((int64_t)b * N * p.Hq + h) * D + my_q * sQ;

@@ -39,7 +39,7 @@
  * this interface.
  *
  * Limits.  d in {64, 128}; B, Hq, Hkv, N >= 1; Hq % Hkv == 0;
- * N * max(Hq, Hkv) * d < 2^31 (elements per batch entry of one tensor);
+ * (N + 256) * max(Hq, Hkv) * d < 2^29 (elements per batch entry of one tensor);
  * B * Hq * ceil(N / 128) < 2^31.
  */
 #ifndef FA_H
