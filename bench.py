@@ -74,8 +74,9 @@ def cpu_baseline(w, seconds: float):
     bb, hh, ii = np.meshgrid(np.arange(w.B), np.arange(w.Hq), np.arange(w.N), indexing="ij")
     rows = np.stack([bb.ravel(), hh.ravel(), ii.ravel()], axis=1)   # every query row
     threads = oracle.host_threads()
-    # calibrate on a small slice, then size the sample to about `seconds`
-    probe = rows[:: max(1, len(rows) // (8 * threads))][: 4 * threads]
+    # calibrate on 1024 evenly strided rows, then size the sample to about
+    # `seconds` (every row when the whole workload fits)
+    probe = rows[np.linspace(0, len(rows) - 1, min(1024, len(rows))).astype(int)]
     t0 = time.perf_counter()
     oracle.attention(q, k, v, w.scale, w.causal, rows=probe, threads=threads)
     dt = max(time.perf_counter() - t0, 1e-3)

@@ -3,7 +3,7 @@
 //
 // Algorithm: the Q-block-outer loop of FlashAttention-2 ("[Attention优化]
 // 从Online-Softmax到FlashAttention V1/V2/V3", section 0x05; "Flash-attention
-// 学习", section 2.2): a workgroup owns 128 query rows of one (batch, head),
+// 学习", section 2.2): a workgroup owns 256 query rows of one (batch, head),
 // keeps them in registers, and streams every visible 64-key K/V tile through
 // LDS once.  Each tile is merged with the online-softmax recurrence
 // ("FlashAttention：IO 感知的精确注意力", section 5): running row maximum m,
@@ -14,13 +14,20 @@
 // for the mask (first page, section 0x09).  Grouped-query attention reads the
 // shared K/V head by index (same section).
 //
-// Work partition inside the workgroup: four wavefronts share each K/V tile
+// Work partition inside the workgroup: eight wavefronts share each K/V tile
 // and each owns 32 whole query rows, so row statistics never cross
 // wavefronts (the "sliced-Q" partition the pages credit to FlashAttention-2).
+// The eight wavefronts form two groups of four, one wavefront of each group
+// per SIMD, that run the same tile sequence one phase apart: while one
+// group issues the matrix-core products of its tile, the other runs the
+// softmax of its previous tile on the vector ALU, and they swap at every
+// barrier.  This is the overlap of softmax with matrix products that the
+// second page (section 10) describes for FlashAttention-3 ("ping-pong"),
+// built from CDNA barriers instead of Hopper warp specialisation.
 //
 // Data movement: K and V tiles go from HBM straight into LDS with 16-byte
-// buffer loads (buffer_load_dwordx4 ... lds), double-buffered so that tile
-// j+1 streams in while tile j is computed.  The buffer descriptor's range
+// buffer loads (buffer_load_dwordx4 ... lds), double-buffered so that the
+// next tile streams in during the two phases that consume the current one.  The buffer descriptor's range
 // check returns zeros for keys past the end of the sequence, so no address
 // ever leaves the tensors.  Both tiles keep their natural [key][d] layout,
 // with the 16-byte chunks of each row permuted by an XOR of the row index so
@@ -68,10 +75,12 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr int kBM = kBlockM;   // query rows per workgroup
+constexpr int kBM = 256;       // query rows per workgroup: 8 wavefronts x 32
 constexpr int kBN = 64;        // keys per K/V tile
-constexpr int kThreads = 256;  // 4 wavefronts of 64
+constexpr int kThreads = 512;  // 8 wavefronts of 64
 constexpr float kLazyLog2 = 8.0f;
+constexpr int PF_PV = 4;       // products whose V^T operands are read ahead of the matrix cores
+constexpr int PF_QK = 4;       // products whose K operands are read ahead of the matrix cores
 constexpr float kLn2 = 0.693147180559945309f;
 
 __device__ __forceinline__ f32x16_t mfma_bf16(u32x4_t a, u32x4_t b, f32x16_t c)
@@ -137,7 +146,7 @@ __device__ __forceinline__ void lds_wait_vm()
 }
 
 template <int D, bool CAUSAL>
-__global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p)
+__global__ void __launch_bounds__(kThreads, 1) fwd_bf16_kernel(FwdParams p)
 {
     constexpr int KSTEPS = D / 16;                 // K-steps of S^T = K Q^T
     constexpr int XB = D / 32;                     // 32-row blocks of O^T
@@ -147,14 +156,15 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p)
     constexpr int ROW_BYTES = D * 2;
     constexpr int ROWS_PER_BLK = 1024 / ROW_BYTES; // rows per 1 KB direct-load block
     constexpr int BLKS = kBN * ROW_BYTES / 1024;   // 1 KB blocks per tile and tensor
-    constexpr int BLKS_PER_WAVE = BLKS / (kThreads / 64);
+    constexpr int NWAVES = kThreads / 64;
+    constexpr int BLKS_PER_WAVE = BLKS / NWAVES;
     constexpr int TILE_ELEMS = kBN * D;
-    static_assert(BLKS_PER_WAVE >= 1, "tile shape");
+    static_assert(BLKS_PER_WAVE >= 1 && BLKS % NWAVES == 0, "tile shape");
 
-    // Two stages of K and V as four distinct objects: the loop below names
-    // each stage statically, so the compiler can see that the loads filling
-    // one stage never alias the operand reads of the other and does not make
-    // those reads wait for the loads in flight.
+    // Two stages of K and V as four distinct objects.  Every access below
+    // names its stage statically, so the compiler can see that the loads
+    // filling one stage never alias the operand reads of the other and does
+    // not make those reads wait for the loads in flight.
     __shared__ __attribute__((aligned(1024))) uint16_t Ks0[TILE_ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t Ks1[TILE_ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t Vs0[TILE_ELEMS];
@@ -165,6 +175,7 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p)
     const int hk = h / p.group;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    const int grp = wave >> 2;                    // 0: leading group, 1: trailing group
     const int lq = lane & 31, hf = lane >> 5;
     const int N = p.N;
     const int q_first = tile * kBM;
@@ -199,25 +210,31 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p)
             for (int e = 0; e < 4; ++e) qreg[t][e] = (qreg[t][e] ^ flip) & keep;
     }
 
-    // ---- number of K/V tiles this workgroup visits
-    int nkt = (N + kBN - 1) / kBN;
-    if (CAUSAL) {
-        const int last_q = min(q_first + kBM, N) - 1;
-        nkt = last_q / kBN + 1;
-    }
+    // ---- K/V tiles this workgroup visits
+    int n = (N + kBN - 1) / kBN;
+    if (CAUSAL) n = (min(q_first + kBM, N) - 1) / kBN + 1;
+    // Tile j holds a key this wavefront can see (causal: keys <= its last row).
+    auto visible = [&](int j) { return !CAUSAL || j * kBN <= wq0 + 31; };
 
-    // ---- HBM -> LDS: each wavefront moves BLKS_PER_WAVE 1 KB blocks of K
-    // and of V per tile; lane l fills physical chunk l % CHUNKS of row
-    // l / CHUNKS of its block.
+    // ---- HBM -> LDS: each wavefront moves BLKS_PER_WAVE 1 KB blocks of a
+    // tile; lane l fills physical chunk l % CHUNKS of row l / CHUNKS.
     const int ld_row = lane / CHUNKS, ld_pch = lane % CHUNKS;
-    auto issue_tile = [&](int j, uint16_t *kdst, uint16_t *vdst) {
+    auto load_k = [&](int j, uint16_t *dst) {
 #pragma unroll
         for (int i = 0; i < BLKS_PER_WAVE; ++i) {
             const int blk = wave * BLKS_PER_WAVE + i;
             const int row = blk * ROWS_PER_BLK + ld_row;
             const uint32_t rowoff = (uint32_t)(j * kBN + row) * (uint32_t)(sK * 2);
-            load_lds16(kbase, range, rowoff + ((ld_pch ^ k_swz<D>(row)) * 16), (lds_void_t *)&kdst[blk * 512]);
-            load_lds16(vbase, range, rowoff + ((ld_pch ^ v_swz<D>(row)) * 16), (lds_void_t *)&vdst[blk * 512]);
+            load_lds16(kbase, range, rowoff + ((ld_pch ^ k_swz<D>(row)) * 16), (lds_void_t *)&dst[blk * 512]);
+        }
+    };
+    auto load_v = [&](int j, uint16_t *dst) {
+#pragma unroll
+        for (int i = 0; i < BLKS_PER_WAVE; ++i) {
+            const int blk = wave * BLKS_PER_WAVE + i;
+            const int row = blk * ROWS_PER_BLK + ld_row;
+            const uint32_t rowoff = (uint32_t)(j * kBN + row) * (uint32_t)(sK * 2);
+            load_lds16(vbase, range, rowoff + ((ld_pch ^ v_swz<D>(row)) * 16), (lds_void_t *)&dst[blk * 512]);
         }
     };
 
@@ -237,21 +254,43 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p)
     for (int xb = 0; xb < XB; ++xb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[xb][i] = 0.f;
+    f32x16_t sacc[NKB];        // S^T of the tile whose softmax is next
+    u32x4_t pb[PVSTEPS];       // P^T (bf16) of the tile whose product is next
 
-    issue_tile(0, Ks0, Vs0);
-    lds_wait_vm();
-    __syncthreads();
-
-    // One K/V tile: prefetch tile j+1 into the other stage, compute tile j.
-    auto step = [&](int j, const uint16_t *ksrc, const uint16_t *vsrc, uint16_t *knext, uint16_t *vnext) {
-        if (j + 1 < nkt) issue_tile(j + 1, knext, vnext);
-        const char *ks = (const char *)ksrc;
-        const char *vs = (const char *)vsrc;
-        const int key0 = j * kBN;
-        const bool active = !CAUSAL || key0 <= wq0 + 31;   // some key visible to this wave
-        if (active) {
-            // ---- S^T = K Q^T
-            f32x16_t sacc[NKB];
+    // Matrix-core step for tile j: O^T += V_{j-1}^T P_{j-1}^T, then
+    // S_j^T = K_j Q^T.  No vector-ALU work beyond operand addressing.
+    auto mfma_step = [&](int j, const uint16_t *kcur, const uint16_t *vprev) {
+        if (j >= 1 && visible(j - 1)) {
+            const char *vs = (const char *)vprev;
+#pragma unroll
+            for (int u = 0; u < PVSTEPS; ++u)
+#pragma unroll
+                for (int xb = 0; xb < XB; ++xb) {
+                    u32x4_t a;
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) {
+                        const int row = 16 * u + 4 * r + tr_row;
+                        const int off = row * ROW_BYTES + (((4 * xb + tr_chunk) ^ v_swz<D>(row)) * 16) + tr_byte;
+                        const i16x4_t t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vs + off));
+                        const u32x2_t t2 = __builtin_bit_cast(u32x2_t, t4);
+                        a[2 * r] = t2[0];
+                        a[2 * r + 1] = t2[1];
+                    }
+                    oacc[xb] = mfma_bf16(a, pb[u], oacc[xb]);
+                }
+            // Operand reads run PF_PV products ahead of the matrix cores.
+#pragma unroll
+            for (int i = 0; i < PF_PV; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+            for (int i = 0; i < PVSTEPS * XB - PF_PV; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < PF_PV; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        if (j < n && visible(j)) {
+            const char *ks = (const char *)kcur;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -265,89 +304,116 @@ __global__ void __launch_bounds__(kThreads, 2) fwd_bf16_kernel(FwdParams p)
                     sacc[kb] = mfma_bf16(a, qreg[t], sacc[kb]);
                 }
             }
-            // ---- mask: keys past the end, and keys after the query when causal
-            const bool need_mask = (key0 + kBN > N) || (CAUSAL && key0 + kBN - 1 > wq0);
-            if (need_mask) {
-                const int lim = (CAUSAL ? min(my_q, N - 1) : N - 1) - (key0 + 8 * hf);
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
+            for (int i = 0; i < PF_QK; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if (kb * 32 + 16 * (i >> 3) + (i & 7) > lim) sacc[kb][i] = -INFINITY;
+            for (int i = 0; i < NKB * KSTEPS - PF_QK; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
-            // ---- row maximum of this tile (in-lane, then one exchange)
-            float mx = -INFINITY;
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-            mx = max_halves(mx);
-            const float m_tile = mx * c;
-            const bool grow = m_tile > m_run + kLazyLog2;
-            float alpha = 1.f;
-            if (grow) {
-                alpha = __builtin_amdgcn_exp2f(m_run - m_tile);   // 0 on the first visit
-                m_run = m_tile;
-            }
-            const float m_sub = m_run == -INFINITY ? 0.f : m_run;
-            // ---- P = 2^(s*c - m); fp32 row sum (for the log-sum-exp)
-            float rf0 = 0.f, rf1 = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; i += 2) {
-                    sacc[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], c, -m_sub));
-                    sacc[kb][i + 1] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i + 1], c, -m_sub));
-                    rf0 += sacc[kb][i];
-                    rf1 += sacc[kb][i + 1];
-                }
-            l_run = l_run * alpha + (rf0 + rf1);
-            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-                for (int xb = 0; xb < XB; ++xb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) oacc[xb][i] *= alpha;
-            }
-            // ---- O^T += V^T P^T.  A second row sum is taken over the same
-            // bf16-rounded probabilities the product consumes (two per
-            // v_dot2_f32_bf16 against (1, 1)) and normalises O, so that
-            // O = sum p v / sum p stays a convex combination of the V rows;
-            // the fp32 sum above gives the log-sum-exp.
-            float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-            for (int u = 0; u < PVSTEPS; ++u) {
-                const int kb = u >> 1, base = (u & 1) * 8;
-                u32x4_t pb;
-#pragma unroll
-                for (int w = 0; w < 4; ++w)
-                    pb[w] = pack_bf16(sacc[kb][base + 2 * w], sacc[kb][base + 2 * w + 1]);
-                rs0 = sum_bf16x2(pb[0], rs0);
-                rs1 = sum_bf16x2(pb[1], rs1);
-                rs0 = sum_bf16x2(pb[2], rs0);
-                rs1 = sum_bf16x2(pb[3], rs1);
-#pragma unroll
-                for (int xb = 0; xb < XB; ++xb) {
-                    u32x4_t a;
-#pragma unroll
-                    for (int r = 0; r < 2; ++r) {
-                        const int row = 16 * u + 4 * r + tr_row;
-                        const int off = row * ROW_BYTES + (((4 * xb + tr_chunk) ^ v_swz<D>(row)) * 16) + tr_byte;
-                        const i16x4_t t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vs + off));
-                        const u32x2_t t2 = __builtin_bit_cast(u32x2_t, t4);
-                        a[2 * r] = t2[0];
-                        a[2 * r + 1] = t2[1];
-                    }
-                    oacc[xb] = mfma_bf16(a, pb, oacc[xb]);
-                }
-            }
-            lb_run = lb_run * alpha + (rs0 + rs1);
+            for (int i = 0; i < PF_QK; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
-        lds_wait_vm();
+    };
+
+    // Vector-ALU step for tile j: mask (tiles crossing the diagonal or the
+    // end only), tile maximum, reference-maximum update with the rare
+    // accumulator rescale, P = 2^(s*c - m) rounded to bf16 and packed as the
+    // next product's B operand, and both row sums: fp32 over the unrounded
+    // values (the log-sum-exp), and over the bf16 values the product consumes
+    // (two per v_dot2_f32_bf16 against (1, 1)), which normalises O so that O
+    // stays a convex combination of the V rows.
+    auto softmax_step = [&](int j) {
+        if (!visible(j)) return;
+        const int key0 = j * kBN;
+        const bool need_mask = (key0 + kBN > N) || (CAUSAL && key0 + kBN - 1 > wq0);
+        if (need_mask) {
+            const int lim = (CAUSAL ? min(my_q, N - 1) : N - 1) - (key0 + 8 * hf);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (kb * 32 + 16 * (i >> 3) + (i & 7) > lim) sacc[kb][i] = -INFINITY;
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+        mx = max_halves(mx);
+        const float m_tile = mx * c;
+        const bool grow = m_tile > m_run + kLazyLog2;
+        float alpha = 1.f;
+        if (grow) {
+            alpha = __builtin_amdgcn_exp2f(m_run - m_tile);   // 0 on the first visit
+            m_run = m_tile;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+            for (int xb = 0; xb < XB; ++xb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) oacc[xb][i] *= alpha;
+        }
+        const float m_sub = m_run == -INFINITY ? 0.f : m_run;
+        float rf0 = 0.f, rf1 = 0.f, rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+        for (int u = 0; u < PVSTEPS; ++u) {
+            const int kb = u >> 1, base = (u & 1) * 8;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][base + 2 * w], c, -m_sub));
+                const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][base + 2 * w + 1], c, -m_sub));
+                rf0 += e0;
+                rf1 += e1;
+                pb[u][w] = pack_bf16(e0, e1);
+                if (w & 1) rs1 = sum_bf16x2(pb[u][w], rs1);
+                else rs0 = sum_bf16x2(pb[u][w], rs0);
+            }
+        }
+        l_run = l_run * alpha + (rf0 + rf1);
+        lb_run = lb_run * alpha + (rs0 + rs1);
+    };
+
+    // ---- ping-pong schedule.  Global phase t = 0 .. 2n+1, one barrier
+    // after each.  A wavefront of group g runs local step s = t - g: even
+    // s = 2j is the matrix-core step for tile j, odd s = 2j+1 the vector-ALU
+    // step for tile j.  Group 1 trails group 0 by one phase, so on every SIMD
+    // one wavefront issues matrix-core work while the other runs the softmax.
+    // K_j and V_{j-1} are read in phases 2j and 2j+1; K_{j+1} and V_j are
+    // loaded during those two phases into the other stage.
+    load_k(0, Ks0);
+    lds_wait_vm();
+    __syncthreads();
+    const int nphase = 2 * n + 2;
+    auto phase = [&](int t, const uint16_t *kcur, const uint16_t *vprev, uint16_t *knext, uint16_t *vnext) {
+        if (!(t & 1)) {                      // start loading K_{j+1}, V_j
+            const int j = t >> 1;
+            if (j + 1 < n) load_k(j + 1, knext);
+            if (j < n) load_v(j, vnext);
+        }
+        const int s = t - grp;
+        if (s >= 0 && s <= 2 * n) {
+            if (!(s & 1)) {
+                // Matrix-core phases issue first when both wavefronts of a SIMD are ready.
+                __builtin_amdgcn_s_setprio(1);
+                mfma_step(s >> 1, kcur, vprev);
+                __builtin_amdgcn_s_setprio(0);
+            } else {
+                softmax_step(s >> 1);
+            }
+        }
+        if (t & 1) lds_wait_vm();            // K_{j+1}, V_j resident before phase 2j+2
         __syncthreads();
     };
-    for (int j = 0; j < nkt; j += 2) {
-        step(j, Ks0, Vs0, Ks1, Vs1);
-        if (j + 1 < nkt) step(j + 1, Ks1, Vs1, Ks0, Vs0);
+    for (int t = 0; t < nphase; t += 4) {
+        // even j = t/2: K_j in Ks0, V_{j-1} in Vs1; loads go to Ks1, Vs0
+        phase(t, Ks0, Vs1, Ks1, Vs0);
+        phase(t + 1, Ks0, Vs1, Ks1, Vs0);
+        if (t + 2 < nphase) {
+            // odd j: K_j in Ks1, V_{j-1} in Vs0; loads go to Ks0, Vs1
+            phase(t + 2, Ks1, Vs0, Ks0, Vs1);
+            phase(t + 3, Ks1, Vs0, Ks0, Vs1);
+        }
     }
 
     // ---- epilogue: O = O_acc / l (bf16, round to nearest even), lse = m ln2 + ln l
@@ -379,8 +445,10 @@ hipError_t launch_one(const FwdParams &p, hipStream_t stream)
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdParams &p, int d, hipStream_t stream)
+hipError_t launch_fwd_bf16(const FwdParams &p_in, int d, hipStream_t stream)
 {
+    FwdParams p = p_in;
+    p.ntiles = (p.N + kBM - 1) / kBM;
     if (d == 128) return p.causal ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
     return p.causal ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
 }

@@ -170,8 +170,10 @@ hipError_t launch_one(const FwdParams &p, hipStream_t stream)
 
 }  // namespace
 
-hipError_t launch_fwd_f32(const FwdParams &p, int d, hipStream_t stream)
+hipError_t launch_fwd_f32(const FwdParams &p_in, int d, hipStream_t stream)
 {
+    FwdParams p = p_in;
+    p.ntiles = (p.N + kBM - 1) / kBM;
     if (d == 128) return p.causal ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
     return p.causal ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
 }

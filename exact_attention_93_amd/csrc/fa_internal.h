@@ -5,7 +5,7 @@
 
 namespace fa {
 
-// Query rows per workgroup: 4 wavefronts x 32 rows.
+// Smallest number of query rows any kernel gives one workgroup (bounds the grid size).
 constexpr int kBlockM = 128;
 
 struct FwdParams {
@@ -14,7 +14,7 @@ struct FwdParams {
     float *lse;
     int B, Hq, Hkv, N;
     int group;       // Hq / Hkv: query heads sharing one key/value head
-    int ntiles;      // ceil(N / kBlockM)
+    int ntiles;      // query tiles per (batch, head); set by each kernel's launcher
     int causal;
     int xcd_groups;  // 1 when B*Hkv is a multiple of 8 (one XCD per head group)
     int qmode;       // 0: q as given; 1: q negated (scale < 0); 2: q zeroed (scale == 0)
