@@ -79,6 +79,7 @@ constexpr int kBM = 256;       // query rows per workgroup: 8 wavefronts x 32
 constexpr int kBN = 64;        // keys per K/V tile
 constexpr int kThreads = 512;  // 8 wavefronts of 64
 constexpr float kLazyLog2 = 8.0f;
+constexpr float kFarSum = 0x1p64f;   // tile row sum that signals a stale reference maximum
 constexpr int PF_PV = 4;       // products whose V^T operands are read ahead of the matrix cores
 constexpr int PF_QK = 4;       // products whose K operands are read ahead of the matrix cores
 constexpr float kLn2 = 0.693147180559945309f;
@@ -323,24 +324,9 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_bf16_kernel(FwdParams p)
     // values (the log-sum-exp), and over the bf16 values the product consumes
     // (two per v_dot2_f32_bf16 against (1, 1)), which normalises O so that O
     // stays a convex combination of the V rows.
-    auto softmax_step = [&](int j) {
-        if (!visible(j)) return;
-        const int key0 = j * kBN;
-        const bool need_mask = (key0 + kBN > N) || (CAUSAL && key0 + kBN - 1 > wq0);
-        if (need_mask) {
-            const int lim = (CAUSAL ? min(my_q, N - 1) : N - 1) - (key0 + 8 * hf);
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (kb * 32 + 16 * (i >> 3) + (i & 7) > lim) sacc[kb][i] = -INFINITY;
-        }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-        mx = max_halves(mx);
+    // Reference-maximum update for a tile whose raw row maximum is mx, with
+    // the accumulator rescale; returns the factor for the running sums.
+    auto settle = [&](float mx) -> float {
         const float m_tile = mx * c;
         const bool grow = m_tile > m_run + kLazyLog2;
         float alpha = 1.f;
@@ -354,8 +340,21 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_bf16_kernel(FwdParams p)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) oacc[xb][i] *= alpha;
         }
+        return alpha;
+    };
+    auto tile_max = [&]() {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+        return max_halves(mx);
+    };
+    // P = 2^(s*c - m) rounded to bf16 and packed as the next product's B
+    // operand; returns the fp32 row sum of the unrounded values.
+    auto exps = [&]() -> float {
         const float m_sub = m_run == -INFINITY ? 0.f : m_run;
-        float rf0 = 0.f, rf1 = 0.f, rs0 = 0.f, rs1 = 0.f;
+        float rf0 = 0.f, rf1 = 0.f;
 #pragma unroll
         for (int u = 0; u < PVSTEPS; ++u) {
             const int kb = u >> 1, base = (u & 1) * 8;
@@ -366,11 +365,50 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_bf16_kernel(FwdParams p)
                 rf0 += e0;
                 rf1 += e1;
                 pb[u][w] = pack_bf16(e0, e1);
-                if (w & 1) rs1 = sum_bf16x2(pb[u][w], rs1);
-                else rs0 = sum_bf16x2(pb[u][w], rs0);
             }
         }
-        l_run = l_run * alpha + (rf0 + rf1);
+        return rf0 + rf1;
+    };
+
+    // Vector-ALU step for tile j: mask (tiles crossing the diagonal or the
+    // end only), the probabilities against the reference maximum, and both
+    // row sums: fp32 over the unrounded values (the log-sum-exp), and over the
+    // bf16 values the product consumes (two per v_dot2_f32_bf16 against
+    // (1, 1)), which normalises O so that O stays a convex combination of the
+    // V rows.  The reference maximum is set from the exact maximum of the
+    // first tile only; later tiles are exponentiated against it directly,
+    // since any reference gives the same softmax (second page, section 5.1).
+    // Should a row's scores run more than 64 (base 2) above the reference,
+    // its tile sum exceeds 2^64 (or overflows), and that tile is redone with
+    // its own maximum and the usual rescale.
+    auto softmax_step = [&](int j) {
+        if (!visible(j)) return;
+        const int key0 = j * kBN;
+        const bool need_mask = (key0 + kBN > N) || (CAUSAL && key0 + kBN - 1 > wq0);
+        if (need_mask) {
+            const int lim = (CAUSAL ? min(my_q, N - 1) : N - 1) - (key0 + 8 * hf);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (kb * 32 + 16 * (i >> 3) + (i & 7) > lim) sacc[kb][i] = -INFINITY;
+        }
+        float alpha = 1.f;
+        if (j == 0) alpha = settle(tile_max());
+        float rf = exps();
+        if (__builtin_amdgcn_ballot_w64(rf > kFarSum) != 0) {
+            alpha *= settle(tile_max());
+            rf = exps();
+        }
+        float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+        for (int u = 0; u < PVSTEPS; ++u) {
+            rs0 = sum_bf16x2(pb[u][0], rs0);
+            rs1 = sum_bf16x2(pb[u][1], rs1);
+            rs0 = sum_bf16x2(pb[u][2], rs0);
+            rs1 = sum_bf16x2(pb[u][3], rs1);
+        }
+        l_run = l_run * alpha + rf;
         lb_run = lb_run * alpha + (rs0 + rs1);
     };
 

@@ -138,3 +138,25 @@ def test_causal_row_equals_prefix_attention():
         op, lp = gpu_fwd(q[:, : i + 1].contiguous(), k[:, : i + 1].contiguous(), v[:, : i + 1].contiguous(), False, 0.125)
         assert (o[0, i].float() - op[0, i].float()).abs().max() <= 1e-2
         assert (lse[0, :, i] - lp[0, :, i]).abs().max() <= 1e-4 * max(1.0, float(lse[0, :, i].abs().max()))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scores_growing_past_the_reference(dtype, causal):
+    """Scores that climb steeply with the key index: every new tile's maximum
+    sits far (hundreds, base 2) above the running reference, so the kernels
+    must move the reference and rescale on every tile: q = (1, small...),
+    k_j = (j/8 rounded to the input type, small...), so the scores rise by
+    about 8*scale per 64 keys (46 and 460 in base 2 for the two scales); the
+    oracle reads the same rounded values."""
+    say(f"case growing scores dtype={dtype} causal={causal}")
+    N, d = 333, 64
+    q, k, v = rand_inputs(1, N, 2, 1, d, dtype, seed=21)
+    dt = q.dtype
+    q = (q.float() * 0.01).to(dt)
+    k = (k.float() * 0.01).to(dt)
+    q[..., 0] = 1.0
+    k[..., 0] = (torch.arange(N, dtype=torch.float32) / 8.0).view(1, N, 1).to(dt)
+    for scale in (4.0, 40.0):
+        o, lse = gpu_fwd(q, k, v, causal, scale)
+        compare(q, k, v, causal, scale, o, lse, label=f"growing scale={scale}")
