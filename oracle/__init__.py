@@ -45,7 +45,7 @@ def _open(path):
     lib = ctypes.CDLL(path)
     f = lib.oracle_attention
     f.restype = ctypes.c_int
-    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 5 + [
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 6 + [
         ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     return lib
@@ -84,20 +84,22 @@ def _as_f32(x) -> np.ndarray:
 def attention(q, k, v, scale, causal=False, rows=None, threads=None, _lib_override=None):
     """Exact attention forward, fp64, for selected query rows.
 
-    q: [B, N, Hq, d]; k, v: [B, N, Hkv, d] (float32 arrays or bf16/fp32 host
-    tensors).  scale: a float (rounded to float32 first, as the GPU sees it).
+    q: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d] (float32 arrays or bf16/fp32
+    host tensors).  scale: a float (rounded to float32 first, as the GPU sees
+    it).  causal: key j visible to query i iff j <= i + Nk - Nq (bottom-right
+    alignment); a row that sees no key gives O = 0, lse = -inf.
     rows: int array [R, 3] of (b, h, i); None means every row, in (b, h, i)
     order.  Returns (o [R, d] float64, lse [R] float64).
     ``_lib_override`` lets the mutation tests run a deliberately broken copy.
     """
     lib = _lib_override if _lib_override is not None else _load()
     q, k, v = _as_f32(q), _as_f32(k), _as_f32(v)
-    B, N, Hq, d = q.shape
-    Hkv = k.shape[2]
-    if k.shape != (B, N, Hkv, d) or v.shape != k.shape:
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if k.shape != (B, Nk, Hkv, d) or v.shape != k.shape:
         raise ValueError("shape mismatch between q, k and v")
     if rows is None:
-        bb, hh, ii = np.meshgrid(np.arange(B), np.arange(Hq), np.arange(N), indexing="ij")
+        bb, hh, ii = np.meshgrid(np.arange(B), np.arange(Hq), np.arange(Nq), indexing="ij")
         rows = np.stack([bb.ravel(), hh.ravel(), ii.ravel()], axis=1)
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
     R = rows.shape[0]
@@ -106,7 +108,7 @@ def attention(q, k, v, scale, causal=False, rows=None, threads=None, _lib_overri
     sc = float(np.float32(scale))
     nt = threads or host_threads()
     rc = lib.oracle_attention(q.ctypes.data, k.ctypes.data, v.ctypes.data,
-                              B, Hq, Hkv, N, d, sc, int(bool(causal)),
+                              B, Hq, Hkv, Nq, Nk, d, sc, int(bool(causal)),
                               rows.ctypes.data, R, o.ctypes.data, lse.ctypes.data, nt)
     if rc != 0:
         raise RuntimeError(f"oracle_attention failed with code {rc}")

@@ -20,13 +20,15 @@
  * row maximum m and the normaliser l) is returned as lse = m + ln(l), the
  * natural logarithm of the sum of exp over the visible scaled scores.
  *
- * Layout (all contiguous, C order): q [B][N][Hq][d], k and v [B][N][Hkv][d],
- * given as float (bf16 inputs are widened to float exactly by the caller).
- * Arithmetic is entirely in double.
+ * Layout (all contiguous, C order): q [B][Nq][Hq][d], k and v
+ * [B][Nk][Hkv][d], given as float (bf16 inputs are widened to float exactly
+ * by the caller).  Arithmetic is entirely in double.
  *
- * Causal mask: key j is visible to query i iff j <= i (sequence lengths of
- * queries and keys are equal, so the top-left and bottom-right alignments of
- * section 0x09 coincide).
+ * Causal mask, aligned to the bottom-right corner of the score matrix (first
+ * page, section 0x09): key j is visible to query i iff j <= i + (Nk - Nq).
+ * With Nq == Nk this is j <= i.  A query that sees no key (possible when
+ * Nq > Nk) gets an all-zero output row, as that section states, and
+ * lse = -inf (the log of an empty sum).
  */
 #include <math.h>
 #include <pthread.h>
@@ -36,7 +38,7 @@
 
 typedef struct {
     const float *q, *k, *v;
-    int B, Hq, Hkv, N, d;
+    int B, Hq, Hkv, Nq, Nk, d;
     double scale;
     int causal;
     const int32_t *rows; /* triples (b, h, i) */
@@ -54,12 +56,21 @@ static void one_row(const job_t *J, int b, int h, int i, double *s,
     const int d = J->d;
     const int g = J->Hq / J->Hkv;
     const int hk = h / g;
-    const float *qi = J->q + (((int64_t)b * J->N + i) * J->Hq + h) * d;
-    const int nvis = J->causal ? i + 1 : J->N;
+    const float *qi = J->q + (((int64_t)b * J->Nq + i) * J->Hq + h) * d;
+    int nvis = J->Nk;                       /* visible keys are 0 .. nvis-1 */
+    if (J->causal) {
+        const int64_t last = (int64_t)i + (J->Nk - J->Nq);
+        nvis = last < 0 ? 0 : (last + 1 < J->Nk ? (int)(last + 1) : J->Nk);
+    }
+    if (nvis == 0) {                        /* empty row: zero output */
+        for (int x = 0; x < d; ++x) o_out[x] = 0.0;
+        *lse_out = -INFINITY;
+        return;
+    }
 
     /* scores s_j = scale * <q_i, k_j> for the visible keys */
     for (int j = 0; j < nvis; ++j) {
-        const float *kj = J->k + (((int64_t)b * J->N + j) * J->Hkv + hk) * d;
+        const float *kj = J->k + (((int64_t)b * J->Nk + j) * J->Hkv + hk) * d;
         double acc = 0.0;
         for (int x = 0; x < d; ++x)
             acc += (double)qi[x] * (double)kj[x];
@@ -77,7 +88,7 @@ static void one_row(const job_t *J, int b, int h, int i, double *s,
     for (int x = 0; x < d; ++x) o_out[x] = 0.0;
     for (int j = 0; j < nvis; ++j) {
         const double a = exp(s[j] - m) / l;
-        const float *vj = J->v + (((int64_t)b * J->N + j) * J->Hkv + hk) * d;
+        const float *vj = J->v + (((int64_t)b * J->Nk + j) * J->Hkv + hk) * d;
         for (int x = 0; x < d; ++x)
             o_out[x] += a * (double)vj[x];
     }
@@ -87,7 +98,7 @@ static void one_row(const job_t *J, int b, int h, int i, double *s,
 static void *worker(void *arg)
 {
     job_t *J = (job_t *)arg;
-    double *s = (double *)malloc(sizeof(double) * (size_t)J->N);
+    double *s = (double *)malloc(sizeof(double) * (size_t)J->Nk);
     if (!s) return (void *)1;
     for (;;) {
         int64_t r;
@@ -108,27 +119,28 @@ static void *worker(void *arg)
 
 /*
  * oracle_attention: O and LSE for the listed query rows.
- *   rows: nrows triples (b, h, i); o: nrows*d doubles; lse: nrows doubles.
+ *   q: [B][Nq][Hq][d]; k, v: [B][Nk][Hkv][d].
+ *   rows: nrows triples (b, h, i), i < Nq; o: nrows*d doubles; lse: nrows doubles.
  *   scale: applied to q.k (the caller passes the same float the GPU gets).
  *   nthreads: worker threads (>= 1).
  * Returns 0 on success, -1 on a bad argument, -2 on allocation failure.
  */
 int oracle_attention(const float *q, const float *k, const float *v,
-                     int B, int Hq, int Hkv, int N, int d, double scale,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int d, double scale,
                      int causal, const int32_t *rows, int64_t nrows,
                      double *o, double *lse, int nthreads)
 {
     if (!q || !k || !v || !rows || !o || !lse) return -1;
-    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || d < 1 || Hq % Hkv) return -1;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1 || Hq % Hkv) return -1;
     for (int64_t r = 0; r < nrows; ++r) {
         const int32_t *t = rows + 3 * r;
-        if (t[0] < 0 || t[0] >= B || t[1] < 0 || t[1] >= Hq || t[2] < 0 || t[2] >= N)
+        if (t[0] < 0 || t[0] >= B || t[1] < 0 || t[1] >= Hq || t[2] < 0 || t[2] >= Nq)
             return -1;
     }
     if (nthreads < 1) nthreads = 1;
     job_t J;
     J.q = q; J.k = k; J.v = v;
-    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.N = N; J.d = d;
+    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.Nq = Nq; J.Nk = Nk; J.d = d;
     J.scale = scale; J.causal = causal;
     J.rows = rows; J.nrows = nrows; J.o = o; J.lse = lse;
     J.next = 0;

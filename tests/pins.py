@@ -45,16 +45,20 @@ def brute_decimal(q, k, v, scale, causal, prec=40):
     softmax before the safe form).  Tiny inputs only.
     """
     getcontext().prec = prec
-    B, N, Hq, d = q.shape
-    Hkv = k.shape[2]
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
     g = Hq // Hkv
     sc = Decimal(float(np.float32(scale)))
-    O = np.zeros((B, Hq, N, d))
-    L = np.zeros((B, Hq, N))
+    O = np.zeros((B, Hq, Nq, d))
+    L = np.zeros((B, Hq, Nq))
     for b in range(B):
         for h in range(Hq):
-            for i in range(N):
-                J = range(i + 1) if causal else range(N)
+            for i in range(Nq):
+                # causal: key j kept iff j - i <= Nk - Nq (bottom-right corner)
+                J = [j for j in range(Nk) if not causal or j - i <= Nk - Nq]
+                if not J:
+                    L[b, h, i] = -math.inf
+                    continue
                 w = []
                 for j in J:
                     s = sum(Decimal(float(q[b, i, h, x])) * Decimal(float(k[b, j, h // g, x])) for x in range(d))
@@ -73,17 +77,44 @@ def _full(att, q, k, v, scale, causal):
 
 
 def pin_brute_force(att):
-    for seed, (B, Hq, Hkv, N, d), causal in [
-        (1, (1, 1, 1, 5, 3), False), (2, (1, 2, 1, 7, 4), True),
-        (3, (2, 2, 2, 4, 8), False), (4, (1, 4, 2, 9, 2), True),
+    for seed, (B, Hq, Hkv, Nq, Nk, d), causal in [
+        (1, (1, 1, 1, 5, 5, 3), False), (2, (1, 2, 1, 7, 7, 4), True),
+        (3, (2, 2, 2, 4, 4, 8), False), (4, (1, 4, 2, 9, 9, 2), True),
+        (5, (1, 2, 1, 3, 8, 4), True), (6, (1, 2, 2, 8, 3, 4), True),
+        (7, (2, 1, 1, 1, 6, 3), True), (8, (1, 2, 1, 6, 4, 2), False),
     ]:
-        q = rand((B, N, Hq, d), seed)
-        k = rand((B, N, Hkv, d), seed + 100)
-        v = rand((B, N, Hkv, d), seed + 200)
+        q = rand((B, Nq, Hq, d), seed)
+        k = rand((B, Nk, Hkv, d), seed + 100)
+        v = rand((B, Nk, Hkv, d), seed + 200)
         o, l = _full(att, q, k, v, 0.7, causal)
         ob, lb = brute_decimal(q, k, v, 0.7, causal)
         assert np.max(np.abs(o - ob)) < 1e-12, "O differs from the decimal brute force"
-        assert np.max(np.abs(l - lb)) < 1e-12, "LSE differs from the decimal brute force"
+        fin = np.isfinite(lb)
+        assert np.array_equal(np.isfinite(l), fin), "rows without keys must have lse = -inf"
+        assert np.all(l[~fin] == -math.inf), "rows without keys must have lse = -inf"
+        assert np.max(np.abs(l[fin] - lb[fin])) < 1e-12, "LSE differs from the decimal brute force"
+
+
+def pin_bottom_right_masks(att):
+    """The two causal masks printed for unequal lengths, first page, section 0x09.
+
+    With scale = 0 every kept key gets the same weight, and with v_j the j-th
+    unit vector the output row i is mask[i] / sum(mask[i]), or zero for a row
+    whose mask is all zero.  lse_i = ln(number of kept keys).
+    """
+    gold = read_golden("causal_bottom_right.txt")
+    for name, nq, nk in (("q2_k5", 2, 5), ("q5_k2", 5, 2)):
+        mask = np.array([gold[f"{name}.row{i}"] if nk > 1 else [gold[f"{name}.row{i}"]]
+                         for i in range(nq)], dtype=np.float64).reshape(nq, nk)
+        q = rand((1, nq, 1, nk), 61)
+        k = rand((1, nk, 1, nk), 62)
+        v = np.eye(nk, dtype=np.float32).reshape(1, nk, 1, nk)
+        o, l = _full(att, q, k, v, 0.0, True)
+        for i in range(nq):
+            n = mask[i].sum()
+            want = mask[i] / n if n else np.zeros(nk)
+            assert np.array_equal(o[0, 0, i], want), f"{name}: row {i} does not follow the printed mask"
+            assert l[0, 0, i] == (math.log(n) if n else -math.inf), f"{name}: lse of row {i}"
 
 
 # -------------------------------------------------------------- worked example
@@ -224,6 +255,27 @@ def pin_torch_sdpa(att):
         if causal:
             s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
         assert np.max(np.abs(l - torch.logsumexp(s, dim=-1).numpy())) < 1e-12, "LSE differs from torch logsumexp"
+    # unequal lengths (decode-like and chunked-prefill-like), the bottom-right
+    # causal mask given to sdpa explicitly as a boolean keep-matrix
+    for seed, (B, Hq, Hkv, Nq, Nk, d), causal in [
+        (54, (2, 8, 2, 1, 300, 128), True), (55, (1, 4, 1, 40, 257, 64), True),
+        (56, (1, 2, 2, 70, 33, 32), False),
+    ]:
+        q, k, v = rand((B, Nq, Hq, d), seed), rand((B, Nk, Hkv, d), seed + 1), rand((B, Nk, Hkv, d), seed + 2)
+        sc = 1 / math.sqrt(d)
+        o, l = _full(att, q, k, v, sc, causal)
+        g = Hq // Hkv
+        tq = torch.from_numpy(q).double().permute(0, 2, 1, 3)
+        tk = torch.from_numpy(np.repeat(k, g, axis=2)).double().permute(0, 2, 1, 3)
+        tv = torch.from_numpy(np.repeat(v, g, axis=2)).double().permute(0, 2, 1, 3)
+        keep = torch.ones(Nq, Nk, dtype=torch.bool)
+        if causal:
+            keep = torch.ones(Nq, Nk, dtype=torch.bool).tril(Nk - Nq)
+        ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=keep, scale=float(np.float32(sc)))
+        assert np.max(np.abs(o - ref.numpy())) < 1e-12, "O differs from torch sdpa (fp64, unequal lengths)"
+        s = (torch.matmul(tq, tk.transpose(-1, -2)) * float(np.float32(sc))).masked_fill(~keep, float("-inf"))
+        assert np.max(np.abs(l - torch.logsumexp(s, dim=-1).numpy())) < 1e-12, "LSE differs (unequal lengths)"
 
 
-ALL_PINS = [pin_worked_example, pin_closed_forms, pin_invariants, pin_brute_force, pin_torch_sdpa]
+ALL_PINS = [pin_worked_example, pin_closed_forms, pin_invariants, pin_brute_force, pin_torch_sdpa,
+            pin_bottom_right_masks]

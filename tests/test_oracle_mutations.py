@@ -19,12 +19,16 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "ref.c")
 MUTATIONS = [
     ("dropped_scale", "s[j] = J->scale * acc;", "s[j] = acc;"),
     ("wrong_gqa_index", "const int hk = h / g;", "const int hk = h % J->Hkv;"),
-    ("causal_off_by_one", "J->causal ? i + 1 : J->N", "J->causal ? (i > 0 ? i : 1) : J->N"),
+    ("causal_off_by_one", "nvis = last < 0 ? 0 : (last + 1 < J->Nk ? (int)(last + 1) : J->Nk);",
+     "nvis = last < 0 ? 0 : (last < J->Nk ? (int)(last > 0 ? last : 1) : J->Nk);"),
+    ("causal_top_left", "const int64_t last = (int64_t)i + (J->Nk - J->Nq);", "const int64_t last = (int64_t)i;"),
+    ("empty_row_not_zero", "for (int x = 0; x < d; ++x) o_out[x] = 0.0;\n        *lse_out = -INFINITY;",
+     "for (int x = 0; x < d; ++x) o_out[x] = 1.0;\n        *lse_out = 0.0;"),
     ("lse_dropped_max", "*lse_out = m + log(l);", "*lse_out = log(l);"),
     ("exp_sign", "l += exp(s[j] - m);", "l += exp(m - s[j]);"),
     ("v_for_k", "const float *kj = J->k +", "const float *kj = J->v +"),
     ("v_reversed_coord", "o_out[x] += a * (double)vj[x];", "o_out[x] += a * (double)vj[d - 1 - x];"),
-    ("q_from_key_row", "const float *qi = J->q + (((int64_t)b * J->N + i)", "const float *qi = J->q + (((int64_t)b * J->N + 0)"),
+    ("q_from_key_row", "const float *qi = J->q + (((int64_t)b * J->Nq + i)", "const float *qi = J->q + (((int64_t)b * J->Nq + 0)"),
     ("no_normalise", "const double a = exp(s[j] - m) / l;", "const double a = exp(s[j] - m);"),
     ("max_not_subtracted_in_weights", "const double a = exp(s[j] - m) / l;", "const double a = exp(s[j]) / l;"),
 ]
