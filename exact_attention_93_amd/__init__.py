@@ -7,11 +7,14 @@ torch on the inputs' device and passes raw device pointers and the current
 HIP stream through ctypes.  There is no CPU fallback: if ``libfa.so`` is
 missing or the tensors are not on a GPU, the call raises.
 
-    o, lse = fwd(q, k, v, causal=False, scale=None)
+    o, lse = fwd(q, k, v, causal=False, scale=None, num_splits=1)
 
-q: [B, N, Hq, d]; k, v: [B, N, Hkv, d]; bf16 (-> fa_fwd) or float32
-(-> fa_fwd_f32), contiguous.  o has q's shape and dtype; lse is float32
-[B, Hq, N], the natural log-sum-exp of each row's scaled, masked scores.
+q: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d]; bf16 or float32, contiguous.  o
+has q's shape and dtype; lse is float32 [B, Hq, Nq], the natural
+log-sum-exp of each row's scaled, masked scores.  Equal lengths and one key
+range go to fa_fwd / fa_fwd_f32; unequal lengths (bottom-right causal
+alignment) or a split key sequence go to fa_fwd_splitkv(_f32), with the
+workspace allocated here by torch.
 """
 from __future__ import annotations
 
@@ -21,14 +24,17 @@ import os
 
 from ._build import LIB_PATH
 
-__all__ = ["fwd", "fa_fwd", "fa_fwd_f32", "fa_strerror", "fa_version", "load_library", "FAError",
+__all__ = ["fwd", "fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_splitkv_num_splits",
+           "fa_splitkv_workspace_size", "fa_strerror", "fa_version", "load_library", "FAError",
            "STATUS", "EXPORTS"]
 
 STATUS = {
     "FA_OK": 0, "FA_ERR_NULL": 1, "FA_ERR_SHAPE": 2, "FA_ERR_HEADS": 3, "FA_ERR_HEADDIM": 4,
     "FA_ERR_ALIGN": 5, "FA_ERR_SCALE": 6, "FA_ERR_ALIAS": 7, "FA_ERR_LAUNCH": 8,
+    "FA_ERR_SPLITS": 9, "FA_ERR_WORKSPACE": 10,
 }
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_strerror", "fa_version")
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_splitkv_num_splits",
+           "fa_splitkv_workspace_size", "fa_strerror", "fa_version")
 
 _lib = None
 
@@ -54,6 +60,16 @@ def load_library(path: str = LIB_PATH):
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = args
+    sargs = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [ctypes.c_float, ctypes.c_int, ctypes.c_int,
+             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
+    for name in ("fa_fwd_splitkv", "fa_fwd_splitkv_f32"):
+        f = getattr(lib, name)
+        f.restype = ctypes.c_int
+        f.argtypes = sargs
+    lib.fa_splitkv_num_splits.restype = ctypes.c_int
+    lib.fa_splitkv_num_splits.argtypes = [ctypes.c_int] * 7
+    lib.fa_splitkv_workspace_size.restype = ctypes.c_size_t
+    lib.fa_splitkv_workspace_size.argtypes = [ctypes.c_int] * 7
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_strerror.argtypes = [ctypes.c_int]
     lib.fa_version.restype = ctypes.c_int
@@ -80,8 +96,34 @@ def fa_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, stream) -> int:
     return load_library().fa_fwd_f32(q, k, v, o, lse, B, Hq, Hkv, N, d, float(scale), int(causal), stream)
 
 
-def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, stream=None):
-    """Attention forward through libfa.so.  Returns (o, lse)."""
+def fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, num_splits, ws, ws_bytes,
+                   stream) -> int:
+    return load_library().fa_fwd_splitkv(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, float(scale), int(causal),
+                                         int(num_splits), ws, ws_bytes, stream)
+
+
+def fa_fwd_splitkv_f32(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, num_splits, ws, ws_bytes,
+                       stream) -> int:
+    return load_library().fa_fwd_splitkv_f32(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, float(scale), int(causal),
+                                             int(num_splits), ws, ws_bytes, stream)
+
+
+def fa_splitkv_num_splits(B, Hq, Hkv, Nq, Nk, d, num_splits) -> int:
+    return load_library().fa_splitkv_num_splits(B, Hq, Hkv, Nq, Nk, d, num_splits)
+
+
+def fa_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits) -> int:
+    return load_library().fa_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits)
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, stream=None,
+        num_splits: int = 1, workspace=None):
+    """Attention forward through libfa.so.  Returns (o, lse).
+
+    num_splits: 1 = the whole key sequence per workgroup; n > 1 = at most n
+    key ranges merged afterwards; 0 = the library's choice.  workspace: an
+    optional preallocated uint8 GPU tensor for the split forward.
+    """
     import torch
 
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
@@ -89,8 +131,8 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("fwd: expected 4-D tensors [B, N, H, d]")
     B, N, Hq, d = q.shape
-    Hkv = k.shape[2]
-    if tuple(k.shape) != (B, N, Hkv, d) or tuple(v.shape) != tuple(k.shape):
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Nk, Hkv, d) or tuple(v.shape) != tuple(k.shape):
         raise ValueError(f"fwd: shape mismatch q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("fwd: q, k, v must all be bfloat16 or all float32")
@@ -104,9 +146,20 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
-    entry = fa_fwd if q.dtype == torch.bfloat16 else fa_fwd_f32
-    st = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-               B, Hq, Hkv, N, d, scale, causal, stream.cuda_stream)
+    bf16 = q.dtype == torch.bfloat16
+    if Nk == N and num_splits == 1:
+        entry = fa_fwd if bf16 else fa_fwd_f32
+        st = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                   B, Hq, Hkv, N, d, scale, causal, stream.cuda_stream)
+    else:
+        need = fa_splitkv_workspace_size(B, Hq, Hkv, N, Nk, d, num_splits)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr = workspace.data_ptr() if workspace is not None else 0
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+        entry = fa_fwd_splitkv if bf16 else fa_fwd_splitkv_f32
+        st = entry(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                   B, Hq, Hkv, N, Nk, d, scale, causal, num_splits, ws_ptr, ws_bytes, stream.cuda_stream)
     if st != 0:
         raise FAError(st, fa_strerror(st))
     return out, lse

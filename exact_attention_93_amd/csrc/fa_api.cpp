@@ -1,4 +1,4 @@
-// C ABI of libfa.so: argument validation, then one kernel launch.
+// C ABI of libfa.so: argument validation, then the kernel launches.
 // The operation, layouts, ownership and error behaviour are stated in
 // include/fa.h.  Validation happens before any HIP call, so an invalid call
 // enqueues nothing.
@@ -12,7 +12,8 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 101;  // 0.1.1
+constexpr int kMaxSplits = 256;
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb)
 {
@@ -20,35 +21,84 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb)
     return x < y + nb && y < x + na;
 }
 
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Key range of one split: a multiple of the split quantum, and the number of
+// ranges that are actually used (never more than requested, none empty).
+void split_shape(int Nk, int num_splits, int &split_keys, int &nsplit)
+{
+    const int64_t quanta = cdiv(Nk, fa::kSplitQuantum);
+    const int64_t per = cdiv(quanta, num_splits);
+    split_keys = (int)(per * fa::kSplitQuantum);
+    nsplit = (int)cdiv(quanta, per);
+}
+
+int heuristic_splits(int B, int Hq, int Nq, int Nk)
+{
+    // Enough workgroups for two per compute unit (256 CUs), each range still
+    // at least four 64-key tiles long.
+    const int64_t units = (int64_t)B * Hq * cdiv(Nq, 256);
+    if (units >= 512) return 1;
+    int64_t s = cdiv(512, units);
+    const int64_t max_by_len = cdiv(Nk, 4 * fa::kSplitQuantum);
+    if (s > max_by_len) s = max_by_len;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return s < 1 ? 1 : (int)s;
+}
+
+size_t workspace_bytes_for(int B, int Hq, int Nq, int d, int nsplit)
+{
+    return (size_t)nsplit * B * Hq * Nq * (size_t)(d + 1) * sizeof(float);
+}
+
 int validate_and_fill(const void *q, const void *k, const void *v, void *o, float *lse,
-                      int B, int Hq, int Hkv, int N, int d, float scale, int causal,
-                      size_t elem, fa::FwdParams &p)
+                      int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                      int num_splits, void *ws, size_t ws_bytes, size_t elem, fa::FwdParams &p)
 {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-    if (B < 1 || Hq < 1 || Hkv < 1 || N < 1) return FA_ERR_SHAPE;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
     if (Hq % Hkv != 0) return FA_ERR_HEADS;
     if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-    // 32-bit byte offsets inside one batch entry (also for the up to 255 rows
-    // past N that the kernels' range-checked loads may address), 32-bit grid
-    const int64_t hmax = Hq > Hkv ? Hq : Hkv;
-    if (((int64_t)N + 256) * hmax * d >= ((int64_t)1 << 29)) return FA_ERR_SHAPE;
-    const int64_t ntiles = ((int64_t)N + fa::kBlockM - 1) / fa::kBlockM;
-    if ((int64_t)B * Hq * ntiles >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+    if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_SPLITS;
+    if (num_splits == 0) num_splits = heuristic_splits(B, Hq, Nq, Nk);
+    int split_keys, nsplit;
+    split_shape(Nk, num_splits, split_keys, nsplit);
+    // 32-bit element offsets inside one batch entry (also for the up to 255
+    // rows past the end that the kernels' range-checked loads may address),
+    // 32-bit grids
+    if (((int64_t)Nq + 256) * Hq * d >= ((int64_t)1 << 29)) return FA_ERR_SHAPE;
+    if (((int64_t)Nk + 256) * Hkv * d >= ((int64_t)1 << 29)) return FA_ERR_SHAPE;
+    const int64_t ntiles = cdiv(Nq, fa::kBlockM);
+    if ((int64_t)B * Hq * ntiles * nsplit >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGN;
     if ((uintptr_t)lse & 3) return FA_ERR_ALIGN;
     if (!isfinite(scale)) return FA_ERR_SCALE;
-    const size_t nq = (size_t)B * N * Hq * d * elem;
-    const size_t nk = (size_t)B * N * Hkv * d * elem;
-    const size_t nl = (size_t)B * Hq * N * sizeof(float);
+    const size_t nq = (size_t)B * Nq * Hq * d * elem;
+    const size_t nk = (size_t)B * Nk * Hkv * d * elem;
+    const size_t nl = (size_t)B * Hq * Nq * sizeof(float);
     if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nk) || overlaps(o, nq, v, nk) ||
         overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nk) || overlaps(lse, nl, v, nk) ||
         overlaps(o, nq, lse, nl))
         return FA_ERR_ALIAS;
+    p.o_part = nullptr;
+    p.lse_part = nullptr;
+    if (nsplit > 1) {
+        const size_t need = workspace_bytes_for(B, Hq, Nq, d, nsplit);
+        if (!ws || ws_bytes < need || ((uintptr_t)ws & 15)) return FA_ERR_WORKSPACE;
+        if (overlaps(ws, need, q, nq) || overlaps(ws, need, k, nk) || overlaps(ws, need, v, nk) ||
+            overlaps(ws, need, o, nq) || overlaps(ws, need, lse, nl))
+            return FA_ERR_ALIAS;
+        p.o_part = (float *)ws;
+        p.lse_part = (float *)ws + (size_t)nsplit * B * Hq * Nq * d;
+    }
 
     p.q = q; p.k = k; p.v = v; p.o = o; p.lse = lse;
-    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.N = N;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk;
+    p.off = Nk - Nq;
     p.group = Hq / Hkv;
     p.ntiles = (int)ntiles;
+    p.nsplit = nsplit;
+    p.split_keys = split_keys;
     p.causal = causal ? 1 : 0;
     p.xcd_groups = ((B * Hkv) % 8 == 0) ? 1 : 0;
     // The kernels take a positive base-2 scale.  A negative scale is the same
@@ -68,6 +118,14 @@ int validate_and_fill(const void *q, const void *k, const void *v, void *o, floa
     return FA_OK;
 }
 
+int run(const fa::FwdParams &p, int d, bool bf16, hipStream_t stream)
+{
+    const hipError_t e = bf16 ? fa::launch_fwd_bf16(p, d, stream) : fa::launch_fwd_f32(p, d, stream);
+    if (e != hipSuccess) return FA_ERR_LAUNCH;
+    if (p.nsplit > 1 && fa::launch_combine(p, d, bf16 ? 1 : 0, stream) != hipSuccess) return FA_ERR_LAUNCH;
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -76,18 +134,56 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
            int B, int Hq, int Hkv, int N, int d, float scale, int causal, void *stream)
 {
     fa::FwdParams p;
-    const int st = validate_and_fill(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, 2, p);
-    if (st != FA_OK) return st;
-    return fa::launch_fwd_bf16(p, d, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    const int st = validate_and_fill(q, k, v, o, lse, B, Hq, Hkv, N, N, d, scale, causal, 1,
+                                     nullptr, 0, 2, p);
+    return st != FA_OK ? st : run(p, d, true, (hipStream_t)stream);
 }
 
 int fa_fwd_f32(const float *q, const float *k, const float *v, float *o, float *lse,
                int B, int Hq, int Hkv, int N, int d, float scale, int causal, void *stream)
 {
     fa::FwdParams p;
-    const int st = validate_and_fill(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, 4, p);
-    if (st != FA_OK) return st;
-    return fa::launch_fwd_f32(p, d, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+    const int st = validate_and_fill(q, k, v, o, lse, B, Hq, Hkv, N, N, d, scale, causal, 1,
+                                     nullptr, 0, 4, p);
+    return st != FA_OK ? st : run(p, d, false, (hipStream_t)stream);
+}
+
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   int num_splits, void *workspace, size_t workspace_bytes, void *stream)
+{
+    fa::FwdParams p;
+    const int st = validate_and_fill(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                                     num_splits, workspace, workspace_bytes, 2, p);
+    return st != FA_OK ? st : run(p, d, true, (hipStream_t)stream);
+}
+
+int fa_fwd_splitkv_f32(const float *q, const float *k, const float *v, float *o, float *lse,
+                       int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                       int num_splits, void *workspace, size_t workspace_bytes, void *stream)
+{
+    fa::FwdParams p;
+    const int st = validate_and_fill(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                                     num_splits, workspace, workspace_bytes, 4, p);
+    return st != FA_OK ? st : run(p, d, false, (hipStream_t)stream);
+}
+
+int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || Hq % Hkv != 0) return -FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return -FA_ERR_HEADDIM;
+    if (num_splits < 0 || num_splits > kMaxSplits) return -FA_ERR_SPLITS;
+    if (num_splits == 0) num_splits = heuristic_splits(B, Hq, Nq, Nk);
+    int split_keys, nsplit;
+    split_shape(Nk, num_splits, split_keys, nsplit);
+    return nsplit;
+}
+
+size_t fa_splitkv_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits)
+{
+    const int nsplit = fa_splitkv_num_splits(B, Hq, Hkv, Nq, Nk, d, num_splits);
+    if (nsplit <= 1) return 0;
+    return workspace_bytes_for(B, Hq, Nq, d, nsplit);
 }
 
 const char *fa_strerror(int status)
@@ -95,13 +191,15 @@ const char *fa_strerror(int status)
     switch (status) {
     case FA_OK: return "success";
     case FA_ERR_NULL: return "a required pointer is NULL";
-    case FA_ERR_SHAPE: return "B, Hq, Hkv and N must be >= 1 and within the size limits";
+    case FA_ERR_SHAPE: return "B, Hq, Hkv and the sequence lengths must be >= 1 and within the size limits";
     case FA_ERR_HEADS: return "Hq must be a multiple of Hkv";
     case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_SCALE: return "scale must be finite (and |scale|*log2(e) representable)";
-    case FA_ERR_ALIAS: return "o or lse overlaps an input or each other";
+    case FA_ERR_ALIAS: return "an output or the workspace overlaps an input or another output";
     case FA_ERR_LAUNCH: return "the HIP runtime reported an error for the kernel launch";
+    case FA_ERR_SPLITS: return "num_splits must be in 0..256";
+    case FA_ERR_WORKSPACE: return "workspace missing, smaller than fa_splitkv_workspace_size, or not 16-byte aligned";
     default: return "unknown fa_status";
     }
 }

@@ -69,6 +69,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
@@ -146,7 +147,7 @@ __device__ __forceinline__ void lds_wait_vm()
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(kThreads, 1) fwd_bf16_kernel(FwdParams p)
 {
     constexpr int KSTEPS = D / 16;                 // K-steps of S^T = K Q^T
@@ -171,30 +172,36 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_bf16_kernel(FwdParams p)
     __shared__ __attribute__((aligned(1024))) uint16_t Vs0[TILE_ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t Vs1[TILE_ELEMS];
 
-    int b, h, tile;
-    decode_tile(p, b, h, tile);
+    int b, h, tile, split;
+    decode_tile(p, b, h, tile, split);
     const int hk = h / p.group;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int grp = wave >> 2;                    // 0: leading group, 1: trailing group
     const int lq = lane & 31, hf = lane >> 5;
-    const int N = p.N;
+    const int Nq = p.Nq, Nk = p.Nk, off = p.off;
     const int q_first = tile * kBM;
     const int wq0 = q_first + wave * 32;          // first query row of this wavefront
     const int my_q = wq0 + lq;                    // query row owned by this lane
     const float c = p.c;
 
+    // ---- K/V tiles this workgroup visits: n tiles from key key_lo on
+    int kt_lo, kt_hi;
+    key_tiles<kBN>(p, q_first, kBM, split, kt_lo, kt_hi);
+    const int n = max(0, kt_hi - kt_lo);
+    const int key_lo = kt_lo * kBN;
+
     const int sQ = p.Hq * D, sK = p.Hkv * D;      // row strides (elements)
-    const uint16_t *qbase = (const uint16_t *)p.q + ((int64_t)b * N * p.Hq + h) * D;
-    const uint16_t *kbase = (const uint16_t *)p.k + ((int64_t)b * N * p.Hkv + hk) * D;
-    const uint16_t *vbase = (const uint16_t *)p.v + ((int64_t)b * N * p.Hkv + hk) * D;
-    // Loads cover rows 0..N-1 of this (batch, kv head): anything at or past
-    // row N reads as zero.
-    const int range = N * sK * 2;
+    const uint16_t *qbase = (const uint16_t *)p.q + ((int64_t)b * Nq * p.Hq + h) * D;
+    const uint16_t *kbase = (const uint16_t *)p.k + ((int64_t)b * Nk * p.Hkv + hk) * D + (int64_t)key_lo * sK;
+    const uint16_t *vbase = (const uint16_t *)p.v + ((int64_t)b * Nk * p.Hkv + hk) * D + (int64_t)key_lo * sK;
+    // Loads cover keys key_lo..Nk-1 of this (batch, kv head): anything at or
+    // past key Nk reads as zero.
+    const int range = max(0, Nk - key_lo) * sK * 2;
 
     // ---- Q^T operand: lane (lq, hf) holds q[my_q][16t + 8hf .. +7] for step t
     u32x4_t qreg[KSTEPS];
-    if (my_q < N) {
+    if (my_q < Nq) {
         const u32x4_t *src = (const u32x4_t *)(qbase + my_q * sQ);
 #pragma unroll
         for (int t = 0; t < KSTEPS; ++t) qreg[t] = src[2 * t + hf];
@@ -211,11 +218,10 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_bf16_kernel(FwdParams p)
             for (int e = 0; e < 4; ++e) qreg[t][e] = (qreg[t][e] ^ flip) & keep;
     }
 
-    // ---- K/V tiles this workgroup visits
-    int n = (N + kBN - 1) / kBN;
-    if (CAUSAL) n = (min(q_first + kBM, N) - 1) / kBN + 1;
-    // Tile j holds a key this wavefront can see (causal: keys <= its last row).
-    auto visible = [&](int j) { return !CAUSAL || j * kBN <= wq0 + 31; };
+    // Tile j holds a key this wavefront can see (causal: keys <= its last
+    // row + off).  A wavefront whose rows all lie past the end sees nothing.
+    const bool wave_live = wq0 < Nq;
+    auto visible = [&](int j) { return wave_live && (!CAUSAL || key_lo + j * kBN <= wq0 + 31 + off); };
 
     // ---- HBM -> LDS: each wavefront moves BLKS_PER_WAVE 1 KB blocks of a
     // tile; lane l fills physical chunk l % CHUNKS of row l / CHUNKS.
@@ -383,10 +389,10 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_bf16_kernel(FwdParams p)
     // its own maximum and the usual rescale.
     auto softmax_step = [&](int j) {
         if (!visible(j)) return;
-        const int key0 = j * kBN;
-        const bool need_mask = (key0 + kBN > N) || (CAUSAL && key0 + kBN - 1 > wq0);
+        const int key0 = key_lo + j * kBN;
+        const bool need_mask = (key0 + kBN > Nk) || (CAUSAL && key0 + kBN - 1 > wq0 + off);
         if (need_mask) {
-            const int lim = (CAUSAL ? min(my_q, N - 1) : N - 1) - (key0 + 8 * hf);
+            const int lim = (CAUSAL ? min(my_q + off, Nk - 1) : Nk - 1) - (key0 + 8 * hf);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -419,7 +425,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_bf16_kernel(FwdParams p)
     // one wavefront issues matrix-core work while the other runs the softmax.
     // K_j and V_{j-1} are read in phases 2j and 2j+1; K_{j+1} and V_j are
     // loaded during those two phases into the other stage.
-    load_k(0, Ks0);
+    if (n > 0) load_k(0, Ks0);
     lds_wait_vm();
     __syncthreads();
     const int nphase = 2 * n + 2;
@@ -454,31 +460,58 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_bf16_kernel(FwdParams p)
         }
     }
 
-    // ---- epilogue: O = O_acc / l (bf16, round to nearest even), lse = m ln2 + ln l
+    // ---- epilogue: O = O_acc / l (bf16, round to nearest even), lse = m ln2 + ln l.
+    // A row that saw no key (l = 0) gets O = 0 and lse = -inf.  A split
+    // forward stores O in fp32 and the log-sum-exp of its key range instead.
     const float l_tot = sum_halves(l_run);
     const float lb_tot = sum_halves(lb_run);
-    if (my_q < N) {
-        const float inv = 1.f / lb_tot;
-        uint16_t *orow = (uint16_t *)p.o + ((int64_t)b * N * p.Hq + h) * D + my_q * sQ;
+    if (my_q < Nq) {
+        const bool empty = l_tot == 0.f;
+        const float inv = empty ? 0.f : 1.f / lb_tot;
+        const float lse_row = empty ? -INFINITY : m_run * kLn2 + logf(l_tot);
+        const int64_t row = ((int64_t)split * p.B + b) * p.Hq + h;   // split = 0 unless SPLIT
+        if (SPLIT) {
+            float *orow = p.o_part + (row * Nq + my_q) * D;
 #pragma unroll
-        for (int xb = 0; xb < XB; ++xb)
+            for (int xb = 0; xb < XB; ++xb)
 #pragma unroll
-            for (int gi = 0; gi < 4; ++gi) {
-                const int x = xb * 32 + 8 * gi + 4 * hf;
-                u32x2_t w = {pack_bf16(oacc[xb][4 * gi] * inv, oacc[xb][4 * gi + 1] * inv),
-                             pack_bf16(oacc[xb][4 * gi + 2] * inv, oacc[xb][4 * gi + 3] * inv)};
-                *(u32x2_t *)(orow + x) = w;
-            }
-        if (hf == 0) p.lse[((int64_t)b * p.Hq + h) * N + my_q] = m_run * kLn2 + logf(l_tot);
+                for (int gi = 0; gi < 4; ++gi) {
+                    const int x = xb * 32 + 8 * gi + 4 * hf;
+                    const f32x4_t w = {oacc[xb][4 * gi] * inv, oacc[xb][4 * gi + 1] * inv,
+                                       oacc[xb][4 * gi + 2] * inv, oacc[xb][4 * gi + 3] * inv};
+                    *(f32x4_t *)(orow + x) = w;
+                }
+            if (hf == 0) p.lse_part[row * Nq + my_q] = lse_row;
+        } else {
+            uint16_t *orow = (uint16_t *)p.o + ((int64_t)b * Nq * p.Hq + h) * D + (int64_t)my_q * sQ;
+#pragma unroll
+            for (int xb = 0; xb < XB; ++xb)
+#pragma unroll
+                for (int gi = 0; gi < 4; ++gi) {
+                    const int x = xb * 32 + 8 * gi + 4 * hf;
+                    u32x2_t w = {pack_bf16(oacc[xb][4 * gi] * inv, oacc[xb][4 * gi + 1] * inv),
+                                 pack_bf16(oacc[xb][4 * gi + 2] * inv, oacc[xb][4 * gi + 3] * inv)};
+                    *(u32x2_t *)(orow + x) = w;
+                }
+            if (hf == 0) p.lse[row * Nq + my_q] = lse_row;
+        }
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 hipError_t launch_one(const FwdParams &p, hipStream_t stream)
 {
-    const unsigned grid = (unsigned)p.B * (unsigned)p.Hq * (unsigned)p.ntiles;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream, p);
+    const unsigned grid = (unsigned)p.B * (unsigned)p.Hq * (unsigned)p.ntiles * (unsigned)p.nsplit;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPLIT>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const FwdParams &p, hipStream_t stream)
+{
+    if (p.nsplit > 1)
+        return p.causal ? launch_one<D, true, true>(p, stream) : launch_one<D, false, true>(p, stream);
+    return p.causal ? launch_one<D, true, false>(p, stream) : launch_one<D, false, false>(p, stream);
 }
 
 }  // namespace
@@ -486,9 +519,8 @@ hipError_t launch_one(const FwdParams &p, hipStream_t stream)
 hipError_t launch_fwd_bf16(const FwdParams &p_in, int d, hipStream_t stream)
 {
     FwdParams p = p_in;
-    p.ntiles = (p.N + kBM - 1) / kBM;
-    if (d == 128) return p.causal ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
-    return p.causal ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
+    p.ntiles = (p.Nq + kBM - 1) / kBM;
+    return d == 128 ? launch_d<128>(p, stream) : launch_d<64>(p, stream);
 }
 
 }  // namespace fa

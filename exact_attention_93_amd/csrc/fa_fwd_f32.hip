@@ -33,7 +33,7 @@ __device__ __forceinline__ f32x16_t mfma_f32(float a, float b, f32x16_t c)
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(FwdParams p)
 {
     constexpr int KP = D + 4;              // K row pitch (floats)
@@ -44,34 +44,34 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(FwdParams p)
     __shared__ __attribute__((aligned(16))) float Ks[kBN * KP];
     __shared__ __attribute__((aligned(16))) float Vs[kBN * D];
 
-    int b, h, tile;
-    decode_tile(p, b, h, tile);
+    int b, h, tile, split;
+    decode_tile(p, b, h, tile, split);
     const int hk = h / p.group;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int lq = lane & 31, hf = lane >> 5;
-    const int N = p.N;
+    const int Nq = p.Nq, Nk = p.Nk, off = p.off;
     const int q_first = tile * kBM;
     const int wq0 = q_first + wave * 32;
     const int my_q = wq0 + lq;
     const float c = p.c;
 
     const int sQ = p.Hq * D, sK = p.Hkv * D;
-    const float *qbase = (const float *)p.q + ((int64_t)b * N * p.Hq + h) * D;
-    const float *kbase = (const float *)p.k + ((int64_t)b * N * p.Hkv + hk) * D;
-    const float *vbase = (const float *)p.v + ((int64_t)b * N * p.Hkv + hk) * D;
+    const float *qbase = (const float *)p.q + ((int64_t)b * Nq * p.Hq + h) * D;
+    const float *kbase = (const float *)p.k + ((int64_t)b * Nk * p.Hkv + hk) * D;
+    const float *vbase = (const float *)p.v + ((int64_t)b * Nk * p.Hkv + hk) * D;
 
     // Q^T operand: step (s, e) of the contraction uses d = 8s + 4hf + e.
     f32x4_t qreg[S4];
     const float qmul = p.qmode == 1 ? -1.f : 1.f;
 #pragma unroll
     for (int s = 0; s < S4; ++s) {
-        if (my_q < N && p.qmode != 2) qreg[s] = *(const f32x4_t *)(qbase + my_q * sQ + 8 * s + 4 * hf) * qmul;
+        if (my_q < Nq && p.qmode != 2) qreg[s] = *(const f32x4_t *)(qbase + my_q * sQ + 8 * s + 4 * hf) * qmul;
         else qreg[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    int nkt = (N + kBN - 1) / kBN;
-    if (CAUSAL) nkt = (min(q_first + kBM, N) - 1) / kBN + 1;
+    int kt_lo, kt_hi;
+    key_tiles<kBN>(p, q_first, kBM, split, kt_lo, kt_hi);
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x16_t oacc[XB];
@@ -80,7 +80,7 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(FwdParams p)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[xb][i] = 0.f;
 
-    for (int j = 0; j < nkt; ++j) {
+    for (int j = kt_lo; j < kt_hi; ++j) {
         const int key0 = j * kBN;
         __syncthreads();   // previous tile fully consumed
 #pragma unroll
@@ -89,7 +89,7 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(FwdParams p)
             const int row = idx / (D / 4), col = (idx % (D / 4)) * 4;
             const int key = key0 + row;
             f32x4_t kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-            if (key < N) {
+            if (key < Nk) {
                 kv = *(const f32x4_t *)(kbase + key * sK + col);
                 vv = *(const f32x4_t *)(vbase + key * sK + col);
             }
@@ -97,7 +97,7 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(FwdParams p)
             *(f32x4_t *)&Vs[row * D + col] = vv;
         }
         __syncthreads();
-        if (CAUSAL && key0 > wq0 + 31) continue;   // whole tile above this wave's rows
+        if (wq0 >= Nq || (CAUSAL && key0 > wq0 + 31 + off)) continue;   // no row of this wave sees the tile
 
         f32x16_t sacc;
 #pragma unroll
@@ -108,11 +108,11 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(FwdParams p)
 #pragma unroll
             for (int e = 0; e < 4; ++e) sacc = mfma_f32(a[e], qreg[s][e], sacc);
         }
-        if ((key0 + kBN > N) || (CAUSAL && key0 + kBN - 1 > wq0)) {
+        if ((key0 + kBN > Nk) || (CAUSAL && key0 + kBN - 1 > wq0 + off)) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int key = key0 + 8 * (i >> 2) + 4 * hf + (i & 3);
-                if (!(key < N && (!CAUSAL || key <= my_q))) sacc[i] = -INFINITY;
+                if (!(key < Nk && (!CAUSAL || key <= my_q + off))) sacc[i] = -INFINITY;
             }
         }
         float mx = -INFINITY;
@@ -143,10 +143,16 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(FwdParams p)
         }
     }
 
+    // A row that saw no key (l = 0) gets O = 0 and lse = -inf; a split
+    // forward stores the result of its key range in the partial buffers.
     const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (my_q < N) {
-        const float inv = 1.f / l_tot;
-        float *orow = (float *)p.o + ((int64_t)b * N * p.Hq + h) * D + my_q * sQ;
+    if (my_q < Nq) {
+        const bool empty = l_tot == 0.f;
+        const float inv = empty ? 0.f : 1.f / l_tot;
+        const float lse_row = empty ? -INFINITY : m_run * kLn2 + logf(l_tot);
+        const int64_t row = ((int64_t)split * p.B + b) * p.Hq + h;   // split = 0 unless SPLIT
+        float *orow = SPLIT ? p.o_part + (row * Nq + my_q) * D
+                            : (float *)p.o + ((int64_t)b * Nq * p.Hq + h) * D + (int64_t)my_q * sQ;
 #pragma unroll
         for (int xb = 0; xb < XB; ++xb)
 #pragma unroll
@@ -156,16 +162,24 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(FwdParams p)
                              oacc[xb][4 * gi + 2] * inv, oacc[xb][4 * gi + 3] * inv};
                 *(f32x4_t *)(orow + x) = w;
             }
-        if (hf == 0) p.lse[((int64_t)b * p.Hq + h) * N + my_q] = m_run * kLn2 + logf(l_tot);
+        if (hf == 0) (SPLIT ? p.lse_part : p.lse)[row * Nq + my_q] = lse_row;
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 hipError_t launch_one(const FwdParams &p, hipStream_t stream)
 {
-    const unsigned grid = (unsigned)p.B * (unsigned)p.Hq * (unsigned)p.ntiles;
-    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3(grid), dim3(kThreads), 0, stream, p);
+    const unsigned grid = (unsigned)p.B * (unsigned)p.Hq * (unsigned)p.ntiles * (unsigned)p.nsplit;
+    hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL, SPLIT>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const FwdParams &p, hipStream_t stream)
+{
+    if (p.nsplit > 1)
+        return p.causal ? launch_one<D, true, true>(p, stream) : launch_one<D, false, true>(p, stream);
+    return p.causal ? launch_one<D, true, false>(p, stream) : launch_one<D, false, false>(p, stream);
 }
 
 }  // namespace
@@ -173,9 +187,8 @@ hipError_t launch_one(const FwdParams &p, hipStream_t stream)
 hipError_t launch_fwd_f32(const FwdParams &p_in, int d, hipStream_t stream)
 {
     FwdParams p = p_in;
-    p.ntiles = (p.N + kBM - 1) / kBM;
-    if (d == 128) return p.causal ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
-    return p.causal ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
+    p.ntiles = (p.Nq + kBM - 1) / kBM;
+    return d == 128 ? launch_d<128>(p, stream) : launch_d<64>(p, stream);
 }
 
 }  // namespace fa

@@ -7,52 +7,86 @@ namespace fa {
 
 // Smallest number of query rows any kernel gives one workgroup (bounds the grid size).
 constexpr int kBlockM = 128;
+// Key ranges of a split forward are multiples of this many keys, so every
+// kernel's key tile divides them.
+constexpr int kSplitQuantum = 64;
 
 struct FwdParams {
     const void *q, *k, *v;
     void *o;
     float *lse;
-    int B, Hq, Hkv, N;
-    int group;       // Hq / Hkv: query heads sharing one key/value head
-    int ntiles;      // query tiles per (batch, head); set by each kernel's launcher
+    float *o_part;    // split forward: fp32 partial outputs [nsplit][B][Hq][Nq][d]
+    float *lse_part;  // split forward: partial log-sum-exp   [nsplit][B][Hq][Nq]
+    int B, Hq, Hkv;
+    int Nq, Nk;       // query and key sequence lengths
+    int off;          // Nk - Nq: key j is visible to query i (causal) iff j <= i + off
+    int group;        // Hq / Hkv: query heads sharing one key/value head
+    int ntiles;       // query tiles per (batch, head); set by each kernel's launcher
+    int nsplit;       // key ranges per query tile (1: the whole key sequence)
+    int split_keys;   // keys per range, a multiple of kSplitQuantum
     int causal;
-    int xcd_groups;  // 1 when B*Hkv is a multiple of 8 (one XCD per head group)
-    int qmode;       // 0: q as given; 1: q negated (scale < 0); 2: q zeroed (scale == 0)
-    float c;         // |scale| * log2(e) (positive), or 1 when scale == 0
+    int xcd_groups;   // 1 when B*Hkv is a multiple of 8 (one XCD per head group)
+    int qmode;        // 0: q as given; 1: q negated (scale < 0); 2: q zeroed (scale == 0)
+    float c;          // |scale| * log2(e) (positive), or 1 when scale == 0
 };
 
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdParams &p, int d, hipStream_t stream);
+// Merge of the nsplit partial results into o (bf16 when out_bf16, else fp32) and lse.
+hipError_t launch_combine(const FwdParams &p, int d, int out_bf16, hipStream_t stream);
 
-// Workgroup index -> (batch, query head, query tile).
+// Workgroup index -> (batch, query head, query tile, key range).
 //
 // Workgroups are dealt to the 8 XCDs round-robin by index, so index L runs
 // on XCD L % 8.  When B*Hkv is a multiple of 8, XCD x is given every query
 // tile of the key/value head groups g with g % 8 == x (all query heads that
 // share a K/V head included), so the K/V of a head is fetched into one XCD's
 // L2 only.  Within an XCD, causal tiles go heaviest first (the last query
-// tile sees the most keys), which keeps the tail of the launch short.
-__device__ __forceinline__ void decode_tile(const FwdParams &p, int &b, int &h, int &tile)
+// tile sees the most keys), which keeps the tail of the launch short.  The
+// key ranges of one query tile are adjacent in the order.
+__device__ __forceinline__ void decode_tile(const FwdParams &p, int &b, int &h, int &tile, int &split)
 {
     const int L = blockIdx.x;
     int t;
     if (p.xcd_groups) {
         const int xcd = L & 7, s = L >> 3;
         const int heads_here = (p.B * p.Hkv >> 3) * p.group;
-        t = s / heads_here;
-        const int r = s - t * heads_here;
+        const int per_t = heads_here * p.nsplit;
+        t = s / per_t;
+        int r = s - t * per_t;
+        split = r / heads_here;
+        r -= split * heads_here;
         const int lg = r / p.group, qh = r - lg * p.group;
         const int g = lg * 8 + xcd;
         b = g / p.Hkv;
         h = (g - b * p.Hkv) * p.group + qh;
     } else {
         const int per = p.B * p.Hq;
-        t = L / per;
-        const int r = L - t * per;
+        const int per_t = per * p.nsplit;
+        t = L / per_t;
+        int r = L - t * per_t;
+        split = r / per;
+        r -= split * per;
         b = r / p.Hq;
         h = r - b * p.Hq;
     }
     tile = p.causal ? (p.ntiles - 1 - t) : t;
+}
+
+// Key tiles [lo, hi) of width BN that the workgroup with query rows
+// [q_first, q_first + rows) and key range `split` visits: the range's tiles,
+// cut (causal) after the tile holding the last key its last row can see.
+// hi <= lo means none.
+template <int BN>
+__device__ __forceinline__ void key_tiles(const FwdParams &p, int q_first, int rows, int split, int &lo, int &hi)
+{
+    const int per = p.split_keys / BN;
+    lo = split * per;
+    hi = min((p.Nk + BN - 1) / BN, lo + per);
+    if (p.causal) {
+        const int last = min(q_first + rows, p.Nq) - 1 + p.off;   // last key any row here sees
+        hi = last < 0 ? lo : min(hi, last / BN + 1);
+    }
 }
 
 }  // namespace fa

@@ -8,7 +8,8 @@ Recipe (one CPU generator per workload, seeded with ``seed``): q, k, v are
 drawn in that order with ``torch.randn`` in float32, q is multiplied by
 ``q_std`` (4.0 for the peaked long-context case), and the result is rounded
 to bf16 (round to nearest even) unless the workload is fp32.  Layout is
-[B, N, H, d] contiguous for every tensor.
+[B, N, H, d] contiguous for every tensor (q with the query length, k and v
+with the key length).
 """
 from __future__ import annotations
 
@@ -31,22 +32,46 @@ class Workload:
     causal: bool
     q_std: float
     seed: int
+    Nk: int = 0         # key length; 0 = the query length N
+    splits: int = 1     # key ranges (0 = the library's choice)
+
+    @property
+    def Nkv(self) -> int:
+        return self.Nk or self.N
 
     @property
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.d)
 
     @property
+    def pairs(self) -> float:
+        """(query, key) pairs per head the FLOP count credits.
+
+        Equal lengths: N^2, halved when causal (the conventional count).
+        Unequal lengths: the exact number of visible pairs (bottom-right
+        causal alignment)."""
+        Nq, Nk = self.N, self.Nkv
+        if Nq == Nk:
+            return Nq * Nq / 2 if self.causal else float(Nq * Nq)
+        if not self.causal:
+            return float(Nq * Nk)
+        off = Nk - Nq
+        lo = max(0, -off)                        # first row that sees a key
+        full = max(lo, min(Nq, Nk - off))        # rows from here on see all Nk keys (off >= 0 case)
+        tri = sum(range(lo + off + 1, full + off + 1)) if full > lo else 0
+        return float(tri + (Nq - full) * Nk)
+
+    @property
     def flops(self) -> float:
-        """4*B*Hq*N^2*d, halved when causal (the conventional count)."""
-        f = 4.0 * self.B * self.Hq * self.N * self.N * self.d
-        return f / 2 if self.causal else f
+        """4*d FLOPs per credited (query, key) pair per head and batch entry."""
+        return 4.0 * self.B * self.Hq * self.pairs * self.d
 
     @property
     def io_bytes(self) -> int:
         """Bytes the forward must move at least once: q, k, v read, o and lse written."""
         s = 4 if self.dtype == "fp32" else 2
-        return (2 * self.Hq + 2 * self.Hkv) * self.B * self.N * self.d * s + 4 * self.B * self.Hq * self.N
+        return ((2 * self.Hq * self.N + 2 * self.Hkv * self.Nkv) * self.B * self.d * s
+                + 4 * self.B * self.Hq * self.N)
 
 
 # The five workloads: a tiny fp32 single head, bf16 MHA at d=64, the headline
@@ -61,17 +86,31 @@ WORKLOADS = {
 ORDER = list(WORKLOADS)
 HEADLINE = "causal_bf16_B2_H32_N4096_d128"
 
+# Split-key workloads (query length != key length), on the head shape of the
+# grouped-query case: one decoding step (one query row per head against a
+# 32K-key cache; the query sees every key under the bottom-right causal
+# alignment) and a chunked prefill (1024 new queries against 16K keys).
+SPLIT_WORKLOADS = {
+    "decode_bf16_B1_Hq32_Hkv8_Nk32768_d128": Workload(
+        "decode_bf16_B1_Hq32_Hkv8_Nk32768_d128", 1, 32, 8, 1, 128, "bf16", True, 1.0, 1006, Nk=32768, splits=0),
+    "chunk_causal_bf16_B1_H32_Nq1024_Nk16384_d128": Workload(
+        "chunk_causal_bf16_B1_H32_Nq1024_Nk16384_d128", 1, 32, 32, 1024, 128, "bf16", True, 1.0, 1007,
+        Nk=16384, splits=0),
+}
+ALL_WORKLOADS = {**WORKLOADS, **SPLIT_WORKLOADS}
 
-def make(B, Hq, Hkv, N, d, dtype="bf16", causal=False, q_std=1.0, seed=0, name="custom") -> Workload:
-    return Workload(name, B, Hq, Hkv, N, d, dtype, causal, q_std, seed)
+
+def make(B, Hq, Hkv, N, d, dtype="bf16", causal=False, q_std=1.0, seed=0, name="custom", Nk=0,
+         splits=1) -> Workload:
+    return Workload(name, B, Hq, Hkv, N, d, dtype, causal, q_std, seed, Nk, splits)
 
 
 def gen_inputs(w: Workload):
     """(q, k, v) on the host, drawn as described in the module docstring."""
     g = torch.Generator(device="cpu").manual_seed(w.seed)
     q = torch.randn((w.B, w.N, w.Hq, w.d), generator=g, dtype=torch.float32)
-    k = torch.randn((w.B, w.N, w.Hkv, w.d), generator=g, dtype=torch.float32)
-    v = torch.randn((w.B, w.N, w.Hkv, w.d), generator=g, dtype=torch.float32)
+    k = torch.randn((w.B, w.Nkv, w.Hkv, w.d), generator=g, dtype=torch.float32)
+    v = torch.randn((w.B, w.Nkv, w.Hkv, w.d), generator=g, dtype=torch.float32)
     if w.q_std != 1.0:
         q = q * w.q_std
     if w.dtype == "bf16":

@@ -16,18 +16,24 @@
  * (same page, section 5.1): tiles of Q, K and V are merged with the
  * online-softmax recurrence, and the N x N score matrix never reaches memory.
  *
- * Causal mask (causal != 0): key j is visible to query i iff j <= i.  Query
- * and key sequences have the same length N, so the top-left and bottom-right
- * alignments of the first page's section 0x09 coincide and no row is empty.
+ * Causal mask (causal != 0), aligned to the bottom-right corner of the
+ * score matrix as the first page's section 0x09 states for unequal lengths:
+ * key j is visible to query i iff j <= i + (Nk - Nq).  With one length N
+ * (fa_fwd, fa_fwd_f32) this is j <= i.  A query row that sees no key (only
+ * possible when Nq > Nk) gets an all-zero output row, as that section says,
+ * and lse = -inf.
  *
  * Layout.  All tensors are dense, contiguous, row-major (C order):
- *     q, o : [B][N][Hq][d]      k, v : [B][N][Hkv][d]      lse : [B][Hq][N]
- * Element (b,n,h,x) of q is at ((b*N + n)*Hq + h)*d + x.
+ *     q, o : [B][Nq][Hq][d]     k, v : [B][Nk][Hkv][d]     lse : [B][Hq][Nq]
+ * Element (b,n,h,x) of q is at ((b*Nq + n)*Hq + h)*d + x.  fa_fwd and
+ * fa_fwd_f32 take one length N = Nq = Nk.
  *
  * Ownership.  Every pointer is a DEVICE pointer owned by the caller.  The
  * library allocates nothing, keeps no state between calls and never
- * synchronises.  It reads q, k, v, writes every element of o and lse, and
- * writes nothing else.  Calls are re-entrant.
+ * synchronises.  It reads q, k, v, writes every element of o and lse (and,
+ * for a split forward, the caller's workspace), and writes nothing else.
+ * Calls are re-entrant; calls that share a workspace must not overlap in
+ * time (enqueue them on one stream).
  *
  * Errors.  Arguments are validated before any HIP call; on a validation error
  * the function returns a nonzero status and enqueues nothing.  On success the
@@ -38,12 +44,14 @@
  * propagate into the results (no check is made).  No C++ exception crosses
  * this interface.
  *
- * Limits.  d in {64, 128}; B, Hq, Hkv, N >= 1; Hq % Hkv == 0;
- * (N + 256) * max(Hq, Hkv) * d < 2^29 (elements per batch entry of one tensor);
- * B * Hq * ceil(N / 128) < 2^31.
+ * Limits.  d in {64, 128}; B, Hq, Hkv, Nq, Nk >= 1; Hq % Hkv == 0;
+ * (Nq + 256) * Hq * d < 2^29 and (Nk + 256) * Hkv * d < 2^29 (elements per
+ * batch entry of one tensor); B * Hq * ceil(Nq / 128) * splits < 2^31.
  */
 #ifndef FA_H
 #define FA_H
+
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -58,7 +66,9 @@ typedef enum {
     FA_ERR_ALIGN = 5,    /* q, k, v or o not 16-byte aligned; lse not 4-byte     */
     FA_ERR_SCALE = 6,    /* scale not finite, or |scale|*log2(e) not a normal float (scale 0 is allowed) */
     FA_ERR_ALIAS = 7,    /* o or lse overlaps q, k, v or each other              */
-    FA_ERR_LAUNCH = 8    /* the HIP runtime reported an error for the launch     */
+    FA_ERR_LAUNCH = 8,   /* the HIP runtime reported an error for the launch     */
+    FA_ERR_SPLITS = 9,   /* num_splits outside 0..256                            */
+    FA_ERR_WORKSPACE = 10 /* split forward: workspace NULL, too small or not 16-byte aligned */
 } fa_status;
 
 /*
@@ -69,6 +79,7 @@ typedef enum {
  *   scale   : a finite float, applied to q.k before the mask; 0 is allowed,
  *             otherwise |scale|*log2(e) must be a normal float.
  *   causal  : 0 = every key visible, nonzero = key j visible iff j <= i.
+ *   (Also reachable as fa_fwd_splitkv with Nq = Nk = N and num_splits = 1.)
  *   stream  : hipStream_t to enqueue on (NULL = null stream).
  * Returns an fa_status value.
  */
@@ -83,6 +94,55 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 int fa_fwd_f32(const float *q, const float *k, const float *v, float *o,
                float *lse, int B, int Hq, int Hkv, int N, int d, float scale,
                int causal, void *stream);
+
+/*
+ * fa_fwd_splitkv -- bf16 attention with separate query and key lengths, the
+ * key sequence optionally split into ranges that run in parallel.
+ *
+ * The keys are cut into num_splits contiguous ranges (multiples of 64 keys,
+ * none empty; fewer ranges are used when Nk is short).  Every range is
+ * processed by its own workgroups, which store for each query row the
+ * softmax over that range applied to its V rows (fp32) and the range's
+ * log-sum-exp; a second kernel then merges the ranges with the online-softmax
+ * rescaling ("FlashAttention：IO 感知的精确注意力", section 5; its section 12.1
+ * describes this split for decoding, where one query row meets a long key
+ * sequence and batch x heads alone cannot fill the GPU).  The result is the
+ * same operation as fa_fwd, up to rounding.
+ *   q, o      : bf16 [B][Nq][Hq][d];  k, v : bf16 [B][Nk][Hkv][d];
+ *   lse       : fp32 [B][Hq][Nq].
+ *   Nq, Nk    : query and key lengths (causal alignment as above).
+ *   num_splits: 1 = no split (workspace unused, may be NULL); 2..256 = at
+ *               most that many ranges; 0 = chosen by fa_splitkv_num_splits.
+ *   workspace : device memory of at least fa_splitkv_workspace_size(...)
+ *               bytes, 16-byte aligned, owned by the caller; its contents on
+ *               entry do not matter and are overwritten.
+ * Other arguments, errors and limits as for fa_fwd.
+ */
+int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *lse,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                   int causal, int num_splits, void *workspace,
+                   size_t workspace_bytes, void *stream);
+
+/* fa_fwd_splitkv with fp32 inputs, output and arithmetic. */
+int fa_fwd_splitkv_f32(const float *q, const float *k, const float *v, float *o,
+                       float *lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                       float scale, int causal, int num_splits, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/*
+ * Number of key ranges fa_fwd_splitkv uses for these arguments (num_splits
+ * as passed to it; 0 picks enough ranges for about two workgroups per
+ * compute unit, each range at least 256 keys).  Returns a value >= 1, or
+ * minus an fa_status for invalid arguments.
+ */
+int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
+
+/*
+ * Workspace bytes fa_fwd_splitkv needs for these arguments:
+ * ranges * B * Hq * Nq * (d + 1) * 4 (partial outputs, then partial
+ * log-sum-exps), or 0 when one range is used or the arguments are invalid.
+ */
+size_t fa_splitkv_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
 
 /* Human-readable text for an fa_status value (static storage, never NULL). */
 const char *fa_strerror(int status);

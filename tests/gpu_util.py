@@ -21,10 +21,10 @@ def say(*a):
     sys.stdout.flush()
 
 
-def gpu_fwd(q, k, v, causal, scale):
+def gpu_fwd(q, k, v, causal, scale, num_splits=1):
     """q, k, v: host tensors.  Returns host (o, lse) from libfa.so."""
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
-    o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=scale)
+    o, lse = fa.fwd(qd, kd, vd, causal=causal, scale=scale, num_splits=num_splits)
     torch.cuda.synchronize()
     return o.cpu(), lse.cpu()
 
@@ -47,6 +47,14 @@ def compare(q, k, v, causal, scale, o, lse, rows=None, kind=None, label="", exac
         r = np.asarray(rows)
         go = o.float().numpy()[r[:, 0], r[:, 2], r[:, 1]].astype(np.float64)
         gl = lse.numpy()[r[:, 0], r[:, 1], r[:, 2]].astype(np.float64)
+    # rows that see no key: O exactly 0 and lse exactly -inf on both sides
+    empty = np.isneginf(rl)
+    if empty.any():
+        say(f"[parity] {label}: {int(empty.sum())} row(s) without visible keys")
+        assert np.all(np.isneginf(gl[empty])), "a row without keys must have lse = -inf"
+        assert np.all(go[empty] == 0.0), "a row without keys must have a zero output"
+    gl = np.where(empty, 0.0, gl)
+    rl = np.where(empty, 0.0, rl)
     err = np.abs(go - ro)
     lerr = np.abs(gl - rl) / np.maximum(1.0, np.abs(rl))
     mx, mean, lmx = float(err.max()), float(err.mean()), float(lerr.max())
@@ -85,14 +93,15 @@ def plain_fp32_error(q, k, v, causal, scale, ro, rows):
     """Error of softmax(scale Q K^T) V evaluated in float32 on the CPU (torch),
     against the fp64 oracle values ro; (max, mean)."""
     B, N, Hq, d = q.shape
+    Nk = k.shape[1]
     g = Hq // k.shape[2]
     qt = q.float().permute(0, 2, 1, 3)
     kt = k.float().repeat_interleave(g, dim=2).permute(0, 2, 3, 1).contiguous()
     vt = v.float().repeat_interleave(g, dim=2).permute(0, 2, 1, 3).contiguous()
     s = torch.matmul(qt, kt) * np.float32(scale)
-    if causal:
-        s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
-    o = torch.matmul(torch.softmax(s, dim=-1), vt)            # [B, Hq, N, d]
+    if causal:   # bottom-right alignment: key j kept iff j - i <= Nk - N
+        s = s.masked_fill(~torch.ones(N, Nk, dtype=torch.bool).tril(Nk - N), float("-inf"))
+    o = torch.nan_to_num(torch.matmul(torch.softmax(s, dim=-1), vt), nan=0.0)   # [B, Hq, N, d]
     if rows is None:
         o = o.reshape(-1, d)
     else:
@@ -102,10 +111,11 @@ def plain_fp32_error(q, k, v, causal, scale, ro, rows):
     return float(e.max()), float(e.mean())
 
 
-def rand_inputs(B, N, Hq, Hkv, d, dtype, seed, q_std=1.0):
+def rand_inputs(B, N, Hq, Hkv, d, dtype, seed, q_std=1.0, Nk=None):
+    Nk = N if Nk is None else Nk
     g = torch.Generator().manual_seed(seed)
     q = torch.randn((B, N, Hq, d), generator=g) * q_std
-    k = torch.randn((B, N, Hkv, d), generator=g)
-    v = torch.randn((B, N, Hkv, d), generator=g)
+    k = torch.randn((B, Nk, Hkv, d), generator=g)
+    v = torch.randn((B, Nk, Hkv, d), generator=g)
     dt = torch.float32 if dtype == "fp32" else torch.bfloat16
     return q.to(dt).contiguous(), k.to(dt).contiguous(), v.to(dt).contiguous()

@@ -46,8 +46,8 @@ def test_status_codes_match_header():
 
 
 def test_version_and_strerror(lib):
-    assert fa.fa_version() == 100
-    for st in range(9):
+    assert fa.fa_version() == 101
+    for st in range(11):
         assert fa.fa_strerror(st)
     assert "unknown" in fa.fa_strerror(99)
 
@@ -91,3 +91,63 @@ def test_python_wrapper_rejects_host_tensors():
     x = torch.zeros(1, 8, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fwd(x, x, x)
+
+
+W = 0x60000000   # fake workspace address
+SGOOD = dict(B=2, Hq=4, Hkv=2, Nq=16, Nk=300, d=64, scale=0.125, causal=1, ns=3)
+
+
+def scall(entry, q=Q, k=K, v=V, o=O, lse=L, ws=W, ws_bytes=1 << 24, **kw):
+    a = dict(SGOOD)
+    a.update(kw)
+    return entry(q, k, v, o, lse, a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"],
+                 a["ns"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("entry", [fa.fa_fwd_splitkv, fa.fa_fwd_splitkv_f32], ids=["bf16", "f32"])
+def test_invalid_arguments_split(lib, entry):
+    S = fa.STATUS
+    assert scall(entry, q=None) == S["FA_ERR_NULL"]
+    for bad in (dict(Nq=0), dict(Nk=0), dict(Nk=-1), dict(B=0)):
+        assert scall(entry, **bad) == S["FA_ERR_SHAPE"], bad
+    assert scall(entry, Nk=1 << 20, Hkv=32, Hq=32, d=128) == S["FA_ERR_SHAPE"]
+    assert scall(entry, Nq=1 << 20, Hkv=1, Hq=32, d=128) == S["FA_ERR_SHAPE"]
+    assert scall(entry, Hq=3) == S["FA_ERR_HEADS"]
+    assert scall(entry, d=256) == S["FA_ERR_HEADDIM"]
+    for ns in (-1, 257, 1 << 30):
+        assert scall(entry, ns=ns) == S["FA_ERR_SPLITS"], ns
+    need = fa.fa_splitkv_workspace_size(2, 4, 2, 16, 300, 64, 3)
+    assert scall(entry, ws=None) == S["FA_ERR_WORKSPACE"]
+    assert scall(entry, ws_bytes=need - 1) == S["FA_ERR_WORKSPACE"]
+    assert scall(entry, ws=W + 8) == S["FA_ERR_WORKSPACE"]
+    assert scall(entry, ws=O) == S["FA_ERR_ALIAS"]          # workspace on the output
+    assert scall(entry, ws=K - 64) == S["FA_ERR_ALIAS"]     # workspace running into k
+    assert scall(entry, lse=W) == S["FA_ERR_ALIAS"]
+    # one range needs no workspace, so a NULL one is not an error; keep an
+    # earlier argument invalid so that nothing is launched
+    assert scall(entry, ns=1, ws=None, ws_bytes=0, q=Q + 8) == S["FA_ERR_ALIGN"]
+    assert scall(entry, ns=1, ws=None, ws_bytes=0, scale=float("nan")) == S["FA_ERR_SCALE"]
+
+
+def test_split_shape_helpers(lib):
+    n = fa.fa_splitkv_num_splits
+    w = fa.fa_splitkv_workspace_size
+    # ranges are whole 64-key quanta, none empty: 300 keys = 5 quanta
+    assert n(1, 1, 1, 1, 300, 64, 1) == 1
+    assert n(1, 1, 1, 1, 300, 64, 2) == 2      # 3 + 2 quanta
+    assert n(1, 1, 1, 1, 300, 64, 4) == 3      # 2 + 2 + 1 quanta
+    assert n(1, 1, 1, 1, 300, 64, 5) == 5
+    assert n(1, 1, 1, 1, 300, 64, 200) == 5
+    assert n(1, 1, 1, 1, 64, 64, 8) == 1
+    assert n(1, 1, 1, 1, 65, 64, 8) == 2
+    assert w(1, 1, 1, 1, 300, 64, 1) == 0
+    assert w(2, 4, 2, 16, 300, 64, 3) == 3 * 2 * 4 * 16 * 65 * 4
+    assert w(1, 32, 8, 1, 32768, 128, 64) == 64 * 32 * 129 * 4
+    # the library's choice: decode with few heads splits, a big prefill does not
+    assert n(1, 32, 8, 1, 32768, 128, 0) > 8
+    assert n(2, 32, 32, 4096, 4096, 128, 0) == 1
+    assert n(1, 1, 1, 1, 100, 64, 0) == 1     # too short to split
+    assert n(1, 3, 2, 1, 100, 64, 0) == -fa.STATUS["FA_ERR_SHAPE"]
+    assert n(1, 4, 2, 1, 100, 96, 0) == -fa.STATUS["FA_ERR_HEADDIM"]
+    assert n(1, 4, 2, 1, 100, 64, -2) == -fa.STATUS["FA_ERR_SPLITS"]
+    assert w(1, 3, 2, 1, 100, 64, 4) == 0
