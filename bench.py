@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the exact attention forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one call of fa_fwd (the whole hot path) over the headline workload:
 causal attention, B=2, H=32, N=4096, d=128, bf16 inputs and output, fp32
@@ -17,6 +17,13 @@ per launch from the committed rocprofv3 counter summary, used only while the
 kernel sources still hash to the value recorded there (else null).
 cpu_baseline: the fp64 CPU oracle, timed on this host's cores over a bounded
 sample of the same workload's query rows, in the same unit.
+
+--workload picks another named workload.  The split-key ones (unequal query
+and key lengths) run fa_fwd_splitkv, whose step is two launches (the
+split forward and the merge) with the workspace allocated before timing; a
+workload whose FLOPs per algorithmic byte fall below the machine balance
+(2.5 PFLOP/s / 8 TB/s) is reported in GB/s of algorithmic bytes against the
+HBM peak instead.
 """
 from __future__ import annotations
 
@@ -32,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attn fwd TFLOP/s at N=4096,d=128 causal bf16; % of dense bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak (published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak bandwidth (published)
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "fa_fwd_bf16_causal_B2_H32_N4096_d128_traffic.txt")
 
@@ -64,8 +72,16 @@ def read_traffic():
         return None
 
 
-def cpu_baseline(w, seconds: float):
-    """Time the fp64 oracle on the headline workload's sampled query rows."""
+def visible_keys(w, i):
+    """Keys query row i sees (bottom-right causal alignment), as an array."""
+    import numpy as np
+    if not w.causal:
+        return np.full(len(i), w.Nkv)
+    return np.clip(i + (w.Nkv - w.N) + 1, 0, w.Nkv)
+
+
+def cpu_baseline(w, seconds: float, hbm: bool):
+    """Time the fp64 oracle on the workload's sampled query rows."""
     import numpy as np
     import oracle
     from exact_attention_93_amd import workloads as W
@@ -85,13 +101,19 @@ def cpu_baseline(w, seconds: float):
     t0 = time.perf_counter()
     oracle.attention(q, k, v, w.scale, w.causal, rows=pick, threads=threads)
     dt = time.perf_counter() - t0
-    vis = (pick[:, 2] + 1) if w.causal else np.full(len(pick), w.N)
+    sample = (f"all {n} query rows of {w.name}" if n == len(rows) else
+              f"{n} of the {len(rows)} query rows of {w.name}, evenly strided over (b, h, i)")
+    if hbm:
+        # the sample's share of the algorithmic bytes
+        nbytes = w.io_bytes * n / len(rows)
+        return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+                "sample": sample + f"; fp64 3-pass oracle, {dt:.1f} s wall; bytes counted as the sample's "
+                                   "share of the workload's algorithmic bytes"}
+    vis = visible_keys(w, pick[:, 2])
     flops = float(4.0 * w.d * vis.sum())
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-        "sample": (f"all {n} query rows of {w.name}" if n == len(rows) else
-                   f"{n} of the {len(rows)} query rows of {w.name}, evenly strided over (b, h, i)")
-                  + f"; fp64 3-pass oracle, {dt:.1f} s wall; FLOPs counted as 4*d per visible key",
+        "sample": sample + f"; fp64 3-pass oracle, {dt:.1f} s wall; FLOPs counted as 4*d per visible key",
     }
 
 
@@ -120,12 +142,18 @@ def main():
         sys.exit(1)
     fa.load_library()   # fails loudly if libfa.so is missing
 
-    w = W.WORKLOADS[args.workload or W.HEADLINE]
+    w = W.ALL_WORKLOADS[args.workload or W.HEADLINE]
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev) for t in W.gen_inputs(w))
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    splits = fa.fa_splitkv_num_splits(w.B, w.Hq, w.Hkv, w.N, w.Nkv, w.d, w.splits)
+    if splits < 1:
+        raise SystemExit(f"bench.py: invalid split arguments for {w.name}")
+    ws_bytes = fa.fa_splitkv_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.Nkv, w.d, w.splits)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev) if ws_bytes else None
+    hbm_bound = w.flops / w.io_bytes < PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -138,7 +166,8 @@ def main():
               file=sys.stderr, flush=True)
 
     def step():
-        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream,
+               num_splits=w.splits, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -162,13 +191,20 @@ def main():
         print("bench.py: non-finite output", file=sys.stderr)
         sys.exit(1)
 
-    value = w.flops / (ms_per_step * 1e-3) / 1e12
-    achieved = w.flops / (mean_launch_ms * 1e-3) / 1e12
-    traffic = read_traffic()
+    if hbm_bound:
+        unit, peak, work = "GB/s", PEAK_HBM_GBS, w.io_bytes / 1e9
+    else:
+        unit, peak, work = "TFLOP/s", PEAK_BF16_TFLOPS, w.flops / 1e12
+    value = work / (ms_per_step * 1e-3)
+    achieved = work / (mean_launch_ms * 1e-3)
+    headline = w.name == W.HEADLINE
+    traffic = read_traffic() if headline else None
+    metric = METRIC if headline else (
+        f"attn fwd {unit} on {w.name}" + ("; % of HBM peak" if hbm_bound else "; % of dense bf16 MFMA peak"))
     out = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 2),
-        "unit": "TFLOP/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
@@ -180,16 +216,19 @@ def main():
         "data": "synthetic (seeded randn, bf16 round-to-nearest-even)",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                    "causal": w.causal, "io_dtype": w.dtype, "accumulate": "fp32", "layout": "BNHD",
-                   "flops_per_step": w.flops, "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2)},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                   "flops_per_step": w.flops, "pct_of_peak": round(100 * value / peak, 2)},
+        "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic},
         "timing": {"mean_launch_us": round(mean_launch_ms * 1e3, 2), "min_launch_us": round(min(per) * 1e3, 2),
                    "max_launch_us": round(max(per) * 1e3, 2), "host_wall_s": round(wall, 4),
                    "kernel_source_hash": kernel_source_hash()},
     }
+    if w.Nkv != w.N or splits > 1:
+        out["config"].update({"Nk": w.Nkv, "splits": splits, "algorithmic_bytes_per_step": w.io_bytes})
+        out["dtype"] = "bf16" if w.dtype == "bf16" else "f32"
     if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, hbm_bound)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

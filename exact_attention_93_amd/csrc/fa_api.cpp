@@ -33,17 +33,35 @@ void split_shape(int Nk, int num_splits, int &split_keys, int &nsplit)
     nsplit = (int)cdiv(quanta, per);
 }
 
-int heuristic_splits(int B, int Hq, int Nq, int Nk)
+int heuristic_splits(int B, int Hq, int Hkv, int Nq, int Nk)
 {
-    // Enough workgroups for two per compute unit (256 CUs), each range still
-    // at least four 64-key tiles long.
+    // Aim at one full round of workgroups over the 256 compute units: the
+    // decoding kernel (one workgroup per K/V head and packed row block) gets
+    // ranges of at least 1024 keys; the prefill kernel (one workgroup per
+    // query head and 256 query rows, one per compute unit) takes the range
+    // count with the fewest rounds per unit of work, ranges of at least 256
+    // keys.
+    constexpr int kCUs = 256;
+    const int group = Hq / Hkv;
+    if (fa::use_decode(Nq, group)) {
+        const int64_t units = (int64_t)B * Hkv * cdiv((int64_t)Nq * group, fa::kDecodeRowBlock);
+        int64_t s = cdiv(kCUs, units);
+        const int64_t max_by_len = cdiv(Nk, 1024);
+        if (s > max_by_len) s = max_by_len;
+        if (s > kMaxSplits) s = kMaxSplits;
+        return s < 1 ? 1 : (int)s;
+    }
     const int64_t units = (int64_t)B * Hq * cdiv(Nq, 256);
-    if (units >= 512) return 1;
-    int64_t s = cdiv(512, units);
-    const int64_t max_by_len = cdiv(Nk, 4 * fa::kSplitQuantum);
-    if (s > max_by_len) s = max_by_len;
-    if (s > kMaxSplits) s = kMaxSplits;
-    return s < 1 ? 1 : (int)s;
+    if (units >= kCUs) return 1;
+    int64_t max_s = cdiv(Nk, 4 * fa::kSplitQuantum);
+    if (max_s > kMaxSplits) max_s = kMaxSplits;
+    int best = 1;
+    double best_cost = 1.0 * cdiv(units, kCUs);
+    for (int s = 2; s <= max_s; ++s) {
+        const double cost = (double)cdiv(units * s, kCUs) / s * (1.0 + 0.02 * s);
+        if (cost < best_cost) { best_cost = cost; best = s; }
+    }
+    return best;
 }
 
 size_t workspace_bytes_for(int B, int Hq, int Nq, int d, int nsplit)
@@ -60,7 +78,7 @@ int validate_and_fill(const void *q, const void *k, const void *v, void *o, floa
     if (Hq % Hkv != 0) return FA_ERR_HEADS;
     if (d != 64 && d != 128) return FA_ERR_HEADDIM;
     if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_SPLITS;
-    if (num_splits == 0) num_splits = heuristic_splits(B, Hq, Nq, Nk);
+    if (num_splits == 0) num_splits = heuristic_splits(B, Hq, Hkv, Nq, Nk);
     int split_keys, nsplit;
     split_shape(Nk, num_splits, split_keys, nsplit);
     // 32-bit element offsets inside one batch entry (also for the up to 255
@@ -70,6 +88,8 @@ int validate_and_fill(const void *q, const void *k, const void *v, void *o, floa
     if (((int64_t)Nk + 256) * Hkv * d >= ((int64_t)1 << 29)) return FA_ERR_SHAPE;
     const int64_t ntiles = cdiv(Nq, fa::kBlockM);
     if ((int64_t)B * Hq * ntiles * nsplit >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+    if ((int64_t)B * Hkv * cdiv((int64_t)Nq * (Hq / Hkv), fa::kDecodeRowBlock) * nsplit >= ((int64_t)1 << 31))
+        return FA_ERR_SHAPE;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGN;
     if ((uintptr_t)lse & 3) return FA_ERR_ALIGN;
     if (!isfinite(scale)) return FA_ERR_SCALE;
@@ -120,7 +140,10 @@ int validate_and_fill(const void *q, const void *k, const void *v, void *o, floa
 
 int run(const fa::FwdParams &p, int d, bool bf16, hipStream_t stream)
 {
-    const hipError_t e = bf16 ? fa::launch_fwd_bf16(p, d, stream) : fa::launch_fwd_f32(p, d, stream);
+    hipError_t e;
+    if (!bf16) e = fa::launch_fwd_f32(p, d, stream);
+    else if (fa::use_decode(p.Nq, p.group)) e = fa::launch_decode_bf16(p, d, stream);
+    else e = fa::launch_fwd_bf16(p, d, stream);
     if (e != hipSuccess) return FA_ERR_LAUNCH;
     if (p.nsplit > 1 && fa::launch_combine(p, d, bf16 ? 1 : 0, stream) != hipSuccess) return FA_ERR_LAUNCH;
     return FA_OK;
@@ -173,7 +196,7 @@ int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num
     if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || Hq % Hkv != 0) return -FA_ERR_SHAPE;
     if (d != 64 && d != 128) return -FA_ERR_HEADDIM;
     if (num_splits < 0 || num_splits > kMaxSplits) return -FA_ERR_SPLITS;
-    if (num_splits == 0) num_splits = heuristic_splits(B, Hq, Nq, Nk);
+    if (num_splits == 0) num_splits = heuristic_splits(B, Hq, Hkv, Nq, Nk);
     int split_keys, nsplit;
     split_shape(Nk, num_splits, split_keys, nsplit);
     return nsplit;

@@ -11,9 +11,13 @@
 //     lse = M + ln(sum_r w_r).
 // A row for which every range is empty keeps O = 0 and lse = -inf.
 //
-// One thread handles four consecutive elements of one row; the D/4 threads
-// of a row read its partials as contiguous float4s, and rows are taken in
-// the (batch, head, query) order of the partial buffers.
+// A row's D/4 threads each own four consecutive elements (one float4), and
+// `spl` such thread groups split the ranges of the row between them (range
+// r goes to group r % spl), so that rows with many ranges (decoding) still
+// spread their loads over many threads.  Each group merges its ranges in one
+// pass with a running maximum (the same rescaling again), so all of its
+// loads can be in flight at once; the groups' results are then merged
+// through LDS.  A workgroup holds 256 / (D/4 * spl) rows.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -36,30 +40,64 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
 }
 
 template <int D, bool OUT_BF16>
-__global__ void __launch_bounds__(kThreads) combine_kernel(FwdParams p)
+__global__ void __launch_bounds__(kThreads) combine_kernel(FwdParams p, int spl)
 {
-    constexpr int TPR = D / 4;              // threads per row
-    constexpr int RPB = kThreads / TPR;     // rows per workgroup
+    constexpr int TPR = D / 4;                   // threads per row and range group
     const int tid = threadIdx.x;
+    const int chunk = tid % TPR;
+    const int sl = (tid / TPR) % spl;            // range group
+    const int rloc = tid / (TPR * spl);          // row within the workgroup
+    const int rpb = kThreads / (TPR * spl);
     const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
-    const int64_t row = (int64_t)blockIdx.x * RPB + tid / TPR;
-    const int x = (tid % TPR) * 4;
-    if (row >= rows) return;
+    const int64_t row = (int64_t)blockIdx.x * rpb + rloc;
+    const bool live = row < rows;
+    const int x = chunk * 4;
 
-    float mx = -INFINITY;
-    for (int r = 0; r < p.nsplit; ++r) mx = fmaxf(mx, p.lse_part[r * rows + row]);
+    __shared__ float red_m[kThreads / 16];                   // [row][group]; spl * rpb <= 256 / 16
+    __shared__ float red_w[kThreads / 16];
+    __shared__ __attribute__((aligned(16))) f32x4_t red_o[kThreads];
+
+    // this group's ranges, merged against their running maximum m
+    float m = -INFINITY, wsum = 0.f;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
-    if (mx != -INFINITY) {
-        for (int r = 0; r < p.nsplit; ++r) {
+    if (live) {
+#pragma unroll 4
+        for (int r = sl; r < p.nsplit; r += spl) {
             const float lr = p.lse_part[r * rows + row];
+            const f32x4_t o = *(const f32x4_t *)(p.o_part + (r * rows + row) * D + x);
             if (lr == -INFINITY) continue;
-            const float w = expf(lr - mx);
+            if (lr > m) {
+                const float a = expf(m - lr);                  // 0 while m is -inf
+                acc *= a;
+                wsum *= a;
+                m = lr;
+            }
+            const float w = expf(lr - m);
             wsum += w;
-            acc += w * *(const f32x4_t *)(p.o_part + (r * rows + row) * D + x);
+            acc += w * o;
         }
     }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    red_o[tid] = acc;
+    if (chunk == 0) {
+        red_m[rloc * spl + sl] = m;
+        red_w[rloc * spl + sl] = wsum;
+    }
+    __syncthreads();
+    if (sl != 0 || !live) return;
+    float M = -INFINITY;
+    for (int j = 0; j < spl; ++j) M = fmaxf(M, red_m[rloc * spl + j]);
+    float W = 0.f;
+    acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+        for (int j = 0; j < spl; ++j) {
+            const float mj = red_m[rloc * spl + j];
+            if (mj == -INFINITY) continue;
+            const float a = expf(mj - M);
+            W += a * red_w[rloc * spl + j];
+            acc += a * red_o[tid + j * TPR];
+        }
+    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
     acc *= inv;
 
     // row = (b * Hq + h) * Nq + i; o is [B][Nq][Hq][D], lse is [B][Hq][Nq]
@@ -73,16 +111,19 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(FwdParams p)
     } else {
         *(f32x4_t *)((float *)p.o + o_off) = acc;
     }
-    if (x == 0) p.lse[row] = mx == -INFINITY ? -INFINITY : mx + logf(wsum);
+    if (chunk == 0) p.lse[row] = M == -INFINITY ? -INFINITY : M + logf(W);
 }
 
 template <int D, bool OUT_BF16>
 hipError_t launch_one(const FwdParams &p, hipStream_t stream)
 {
-    constexpr int RPB = kThreads / (D / 4);
+    constexpr int TPR = D / 4;
+    int spl = 1;                                  // range groups: a power of two, at most the ranges
+    while (spl < p.nsplit && spl * 2 * TPR <= kThreads) spl *= 2;
+    const int rpb = kThreads / (TPR * spl);
     const int64_t rows = (int64_t)p.B * p.Hq * p.Nq;
-    const unsigned grid = (unsigned)((rows + RPB - 1) / RPB);
-    hipLaunchKernelGGL((combine_kernel<D, OUT_BF16>), dim3(grid), dim3(kThreads), 0, stream, p);
+    const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
+    hipLaunchKernelGGL((combine_kernel<D, OUT_BF16>), dim3(grid), dim3(kThreads), 0, stream, p, spl);
     return hipGetLastError();
 }
 

@@ -31,6 +31,14 @@ struct FwdParams {
 };
 
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, hipStream_t stream);
+// Few query rows per K/V head (decoding): rows of one head group packed into
+// 32-row blocks, K/V read once per group.
+hipError_t launch_decode_bf16(const FwdParams &p, int d, hipStream_t stream);
+constexpr int kDecodeRowBlock = 32;
+// Packed rows (query rows x query heads per K/V head) up to which the
+// decoding kernel is used for bf16.
+constexpr int kDecodeMaxRows = 64;
+inline bool use_decode(int Nq, int group) { return (int64_t)Nq * group <= kDecodeMaxRows; }
 hipError_t launch_fwd_f32(const FwdParams &p, int d, hipStream_t stream);
 // Merge of the nsplit partial results into o (bf16 when out_bf16, else fp32) and lse.
 hipError_t launch_combine(const FwdParams &p, int d, int out_bf16, hipStream_t stream);

@@ -113,3 +113,30 @@ def test_split_workload(name):
     q, k, v = W.gen_inputs(w)
     o, lse = gpu_fwd(q, k, v, w.causal, w.scale, num_splits=w.splits)
     compare(q, k, v, w.causal, w.scale, o, lse, rows=W.sample_rows(w), label=name, exact_bounds=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("heads_nq", [(1, 1, 1), (4, 1, 1), (8, 1, 2), (32, 8, 1), (16, 1, 4), (8, 2, 16),
+                                      (13, 1, 5), (4, 4, 3)],
+                         ids=lambda t: f"Hq{t[0]}Hkv{t[1]}Nq{t[2]}")
+@pytest.mark.parametrize("splits", [1, 3, 0])
+def test_decode_shapes(heads_nq, causal, d, splits):
+    """Few query rows per K/V head (one or two packed 32-row blocks; 13*5 = 65
+    rows crosses over to the prefill kernel), long ragged key sequences."""
+    Hq, Hkv, Nq = heads_nq
+    Nk = 1000 + 37 * Nq
+    say(f"case decode Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal} d={d} splits={splits}")
+    q, k, v = rand_inputs(2, Nq, Hq, Hkv, d, "bf16", seed=Hq * 100 + Nq + d + splits, Nk=Nk)
+    o, lse = gpu_fwd(q, k, v, causal, 1 / math.sqrt(d), num_splits=splits)
+    compare(q, k, v, causal, 1 / math.sqrt(d), o, lse, label=f"decode Hq={Hq} Hkv={Hkv} Nq={Nq}")
+
+
+def test_decode_rows_without_keys():
+    """More query rows than keys in the decoding kernel: rows i < Nq - Nk see
+    nothing under the bottom-right alignment and must come out zero."""
+    q, k, v = rand_inputs(1, 12, 4, 1, 128, "bf16", seed=5, Nk=7)
+    for splits in (1, 2):
+        o, lse = gpu_fwd(q, k, v, True, 0.1, num_splits=splits)
+        compare(q, k, v, True, 0.1, o, lse, label=f"decode empty rows splits={splits}")
+        assert torch.all(o[0, :5].float() == 0) and torch.all(torch.isneginf(lse[0, :, :5]))
