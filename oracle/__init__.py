@@ -1,4 +1,4 @@
-"""CPU oracle for the exact attention forward.
+"""CPU oracle for the exact attention forward and its gradients.
 
 TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the
 benchmark's CPU-baseline leg are the only users; the GPU library never
@@ -8,6 +8,8 @@ library.
 * :func:`attention` -- the plain definition (3-pass safe softmax, fp64), in C
   (``ref.c``), threaded over query rows.  See the header of ``ref.c`` for the
   passages it follows.
+* :func:`attention_bwd` -- dq, dk, dv: the derivative of that definition for
+  an upstream gradient dO, fp64, in C (``ref.c``), per key/value head group.
 * :mod:`oracle.recurrence` -- the pages' online-softmax / tiled recurrences,
   step by step, in numpy (for the worked-example pins and cross-checks).
 
@@ -48,6 +50,11 @@ def _open(path):
     f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 6 + [
         ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    f = lib.oracle_attention_bwd
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] * 6 + [
+        ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     return lib
 
 
@@ -113,3 +120,35 @@ def attention(q, k, v, scale, causal=False, rows=None, threads=None, _lib_overri
     if rc != 0:
         raise RuntimeError(f"oracle_attention failed with code {rc}")
     return o, lse
+
+
+def attention_bwd(q, k, v, dout, scale, causal=False, groups=None, threads=None, _lib_override=None):
+    """Gradients of the exact attention forward, fp64, per key/value head group.
+
+    q, dout: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d]; scale and causal as in
+    :func:`attention`.  groups: int array [G, 2] of (b, hk); None means every
+    group in (b, hk) order.  Returns (dq [G, Hq/Hkv, Nq, d], dk [G, Nk, d],
+    dv [G, Nk, d]) as float64: dq for the query heads hk*g .. hk*g+g-1 of each
+    group, dk and dv of the shared head summed over them.
+    """
+    lib = _lib_override if _lib_override is not None else _load()
+    q, k, v, dout = _as_f32(q), _as_f32(k), _as_f32(v), _as_f32(dout)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if k.shape != (B, Nk, Hkv, d) or v.shape != k.shape or dout.shape != q.shape:
+        raise ValueError("shape mismatch between q, k, v and dout")
+    if groups is None:
+        bb, hh = np.meshgrid(np.arange(B), np.arange(Hkv), indexing="ij")
+        groups = np.stack([bb.ravel(), hh.ravel()], axis=1)
+    groups = np.ascontiguousarray(np.asarray(groups, dtype=np.int32).reshape(-1, 2))
+    G, g = groups.shape[0], Hq // Hkv
+    dq = np.empty((G, g, Nq, d), dtype=np.float64)
+    dk = np.empty((G, Nk, d), dtype=np.float64)
+    dv = np.empty((G, Nk, d), dtype=np.float64)
+    nt = threads or host_threads()
+    rc = lib.oracle_attention_bwd(q.ctypes.data, k.ctypes.data, v.ctypes.data, dout.ctypes.data,
+                                  B, Hq, Hkv, Nq, Nk, d, float(np.float32(scale)), int(bool(causal)),
+                                  groups.ctypes.data, G, dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, nt)
+    if rc != 0:
+        raise RuntimeError(f"oracle_attention_bwd failed with code {rc}")
+    return dq, dk, dv

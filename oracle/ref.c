@@ -162,3 +162,189 @@ int oracle_attention(const float *q, const float *k, const float *v,
     pthread_mutex_destroy(&J.lock);
     return rc;
 }
+
+/* ------------------------------------------------------------------------
+ * Backward: gradients of the forward above with respect to q, k and v, for
+ * an upstream gradient dout = dL/dO.
+ *
+ * This is the derivative of the definition, written out row by row in
+ * double precision.  For query row i of head h (key/value head hk):
+ *   P_ij  = softmax_j(s_i.) over the visible keys (0 elsewhere)
+ *   dP_ij = <dout_i, v_j>
+ *   dS_ij = P_ij * (dP_ij - sum_k P_ik dP_ik)        (softmax Jacobian)
+ *   dq_i  = scale * sum_j dS_ij k_j
+ *   dk_j += scale * dS_ij q_i,  dv_j += P_ij dout_i  (summed over the rows
+ *                                                     and over the query
+ *                                                     heads of the group)
+ * The pages describe how FlashAttention organises this computation (the
+ * first page, sections 0x04 and 0x05: S and P recomputed from the stored
+ * row statistics, an outer loop over K/V blocks, dQ accumulated across
+ * blocks; the second page, section 6); the gradients themselves are those
+ * of the forward's definition.  A row without visible keys contributes
+ * nothing.
+ *
+ * Work is done per key/value head group (b, hk): dq for the Hq/Hkv query
+ * heads of the group and dk, dv of the shared head.  Threads split the query
+ * rows of a group and keep private dk, dv sums that are added in thread
+ * order at the end (the result does not depend on scheduling).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    const float *q, *k, *v, *dout;
+    int B, Hq, Hkv, Nq, Nk, d;
+    double scale;
+    int causal;
+    int b, hk;              /* the group being processed */
+    int nthreads;
+    double *dq;             /* [g][Nq][d] */
+    double *dk_part;        /* [nthreads][Nk][d] */
+    double *dv_part;
+    int fail;
+} bwd_job_t;
+
+typedef struct {
+    bwd_job_t *J;
+    int t;
+} bwd_arg_t;
+
+static void *bwd_worker(void *arg)
+{
+    bwd_arg_t *A = (bwd_arg_t *)arg;
+    bwd_job_t *J = A->J;
+    const int d = J->d, Nq = J->Nq, Nk = J->Nk;
+    const int g = J->Hq / J->Hkv;
+    double *p = (double *)malloc(sizeof(double) * (size_t)Nk);
+    double *dp = (double *)malloc(sizeof(double) * (size_t)Nk);
+    if (!p || !dp) {
+        free(p);
+        free(dp);
+        J->fail = 1;
+        return NULL;
+    }
+    double *dk = J->dk_part + (size_t)A->t * Nk * d;
+    double *dv = J->dv_part + (size_t)A->t * Nk * d;
+    const int64_t total = (int64_t)g * Nq;
+    for (int64_t r = A->t; r < total; r += J->nthreads) {
+        const int hh = (int)(r / Nq), i = (int)(r % Nq);
+        const int h = J->hk * g + hh;
+        const float *qi = J->q + (((int64_t)J->b * Nq + i) * J->Hq + h) * d;
+        const float *doi = J->dout + (((int64_t)J->b * Nq + i) * J->Hq + h) * d;
+        double *dqi = J->dq + ((int64_t)hh * Nq + i) * d;
+        for (int x = 0; x < d; ++x) dqi[x] = 0.0;
+        int nvis = Nk;
+        if (J->causal) {
+            const int64_t last = (int64_t)i + (Nk - Nq);
+            nvis = last < 0 ? 0 : (last + 1 < Nk ? (int)(last + 1) : Nk);
+        }
+        if (nvis == 0) continue;
+        /* P_i. by the three-pass softmax, and dP_i. */
+        double m = -INFINITY;
+        for (int j = 0; j < nvis; ++j) {
+            const float *kj = J->k + (((int64_t)J->b * Nk + j) * J->Hkv + J->hk) * d;
+            const float *vj = J->v + (((int64_t)J->b * Nk + j) * J->Hkv + J->hk) * d;
+            double s = 0.0, t = 0.0;
+            for (int x = 0; x < d; ++x) {
+                s += (double)qi[x] * (double)kj[x];
+                t += (double)doi[x] * (double)vj[x];
+            }
+            p[j] = J->scale * s;
+            dp[j] = t;
+            if (p[j] > m) m = p[j];
+        }
+        double l = 0.0;
+        for (int j = 0; j < nvis; ++j) {
+            p[j] = exp(p[j] - m);
+            l += p[j];
+        }
+        double pdp = 0.0;
+        for (int j = 0; j < nvis; ++j) {
+            p[j] /= l;
+            pdp += p[j] * dp[j];
+        }
+        for (int j = 0; j < nvis; ++j) {
+            const double ds = p[j] * (dp[j] - pdp);
+            const float *kj = J->k + (((int64_t)J->b * Nk + j) * J->Hkv + J->hk) * d;
+            double *dkj = dk + (int64_t)j * d, *dvj = dv + (int64_t)j * d;
+            for (int x = 0; x < d; ++x) {
+                dqi[x] += J->scale * ds * (double)kj[x];
+                dkj[x] += J->scale * ds * (double)qi[x];
+                dvj[x] += p[j] * (double)doi[x];
+            }
+        }
+    }
+    free(p);
+    free(dp);
+    return NULL;
+}
+
+/*
+ * oracle_attention_bwd: dq, dk, dv for the listed key/value head groups.
+ *   q, dout: [B][Nq][Hq][d]; k, v: [B][Nk][Hkv][d] (float).
+ *   groups: ngroups pairs (b, hk).
+ *   dq: ngroups * (Hq/Hkv) * Nq * d doubles, [group][query head in group][i][x];
+ *   dk, dv: ngroups * Nk * d doubles, [group][j][x].
+ * Returns 0 on success, -1 on a bad argument, -2 on allocation failure.
+ */
+int oracle_attention_bwd(const float *q, const float *k, const float *v, const float *dout,
+                         int B, int Hq, int Hkv, int Nq, int Nk, int d, double scale,
+                         int causal, const int32_t *groups, int64_t ngroups,
+                         double *dq, double *dk, double *dv, int nthreads)
+{
+    if (!q || !k || !v || !dout || !groups || !dq || !dk || !dv) return -1;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1 || Hq % Hkv) return -1;
+    for (int64_t r = 0; r < ngroups; ++r)
+        if (groups[2 * r] < 0 || groups[2 * r] >= B || groups[2 * r + 1] < 0 || groups[2 * r + 1] >= Hkv)
+            return -1;
+    if (nthreads < 1) nthreads = 1;
+    const int g = Hq / Hkv;
+    bwd_job_t J;
+    J.q = q; J.k = k; J.v = v; J.dout = dout;
+    J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.Nq = Nq; J.Nk = Nk; J.d = d;
+    J.scale = scale; J.causal = causal; J.nthreads = nthreads;
+    J.dk_part = (double *)malloc(sizeof(double) * (size_t)nthreads * Nk * d);
+    J.dv_part = (double *)malloc(sizeof(double) * (size_t)nthreads * Nk * d);
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    bwd_arg_t *args = (bwd_arg_t *)malloc(sizeof(bwd_arg_t) * (size_t)nthreads);
+    int rc = 0;
+    if (!J.dk_part || !J.dv_part || !th || !args) rc = -2;
+    for (int64_t r = 0; r < ngroups && rc == 0; ++r) {
+        J.b = groups[2 * r];
+        J.hk = groups[2 * r + 1];
+        J.dq = dq + (size_t)r * g * Nq * d;
+        J.fail = 0;
+        memset(J.dk_part, 0, sizeof(double) * (size_t)nthreads * Nk * d);
+        memset(J.dv_part, 0, sizeof(double) * (size_t)nthreads * Nk * d);
+        int started = 0;
+        for (int t = 0; t < nthreads; ++t) {
+            args[t].J = &J;
+            args[t].t = t;
+        }
+        for (int t = 0; t < nthreads; ++t) {
+            if (pthread_create(&th[t], NULL, bwd_worker, &args[t]) != 0) break;
+            ++started;
+        }
+        if (started < nthreads) {
+            /* run the missing workers' rows here, in order */
+            for (int t = started; t < nthreads; ++t) bwd_worker(&args[t]);
+        }
+        for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
+        if (J.fail) {
+            rc = -2;
+            break;
+        }
+        double *dkg = dk + (size_t)r * Nk * d, *dvg = dv + (size_t)r * Nk * d;
+        for (int64_t e = 0; e < (int64_t)Nk * d; ++e) {
+            double sk = 0.0, sv = 0.0;
+            for (int t = 0; t < nthreads; ++t) {
+                sk += J.dk_part[(size_t)t * Nk * d + e];
+                sv += J.dv_part[(size_t)t * Nk * d + e];
+            }
+            dkg[e] = sk;
+            dvg[e] = sv;
+        }
+    }
+    free(J.dk_part);
+    free(J.dv_part);
+    free(th);
+    free(args);
+    return rc;
+}

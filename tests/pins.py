@@ -279,3 +279,130 @@ def pin_torch_sdpa(att):
 
 ALL_PINS = [pin_worked_example, pin_closed_forms, pin_invariants, pin_brute_force, pin_torch_sdpa,
             pin_bottom_right_masks]
+
+
+# ==================================================================== backward
+# Pins for oracle.attention_bwd.  Each takes (att, bwd) callables with the
+# signatures of oracle.attention and oracle.attention_bwd.
+
+def _full_bwd(bwd, q, k, v, do, scale, causal):
+    """dq [B, Hq, Nq, d], dk and dv [B, Hkv, Nk, d] from the grouped output."""
+    dq, dk, dv = bwd(q, k, v, do, scale, causal)
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    return dq.reshape(B, Hq, Nq, d), dk.reshape(B, Hkv, Nk, d), dv.reshape(B, Hkv, Nk, d)
+
+
+def pin_bwd_finite_differences(att, bwd):
+    """Central differences of L = sum(dO * O) through the forward oracle.
+
+    Each input coordinate is moved by +-h and +-2h (h = 2^-9, exact in
+    float32 for these magnitudes) and the two central differences are
+    combined by Richardson extrapolation (error O(h^4)).  Checks that the
+    gradients are those of the (separately pinned) forward definition,
+    including grouped heads, the bottom-right causal mask and rows that see
+    no key."""
+    h = 2.0 ** -9
+    for seed, (B, Hq, Hkv, Nq, Nk, d), causal in [
+        (71, (1, 2, 1, 4, 6, 3), True), (72, (1, 2, 2, 5, 3, 2), True), (73, (2, 2, 1, 3, 3, 2), False),
+    ]:
+        # inputs on a 2^-20 grid, so that x +- h and x +- 2h are exact in float32
+        q, k, v = (np.round(rand(s_, seed + o_) * 2.0 ** 20) / 2.0 ** 20 for s_, o_ in
+                   (((B, Nq, Hq, d), 0), ((B, Nk, Hkv, d), 1), ((B, Nk, Hkv, d), 2)))
+        q, k, v = q.astype(np.float32), k.astype(np.float32), v.astype(np.float32)
+        do = rand((B, Nq, Hq, d), seed + 3)
+        sc = 0.8
+        dq, dk, dv = _full_bwd(bwd, q, k, v, do, sc, causal)
+
+        def loss(qq, kk, vv):
+            o, _ = att(qq, kk, vv, sc, causal)
+            return float(np.sum(o * do.transpose(0, 2, 1, 3).reshape(-1, d).astype(np.float64)))
+
+        for name, x, grad in (("q", q, dq.transpose(0, 2, 1, 3)), ("k", k, dk.transpose(0, 2, 1, 3)),
+                              ("v", v, dv.transpose(0, 2, 1, 3))):
+            num = np.zeros(x.shape)
+            for idx in np.ndindex(*x.shape):
+                vals = []
+                for step in (h, 2 * h):
+                    xp, xm = x.copy(), x.copy()
+                    xp[idx] += np.float32(step)
+                    xm[idx] -= np.float32(step)
+                    args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+                    args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+                    vals.append((loss(*args_p) - loss(*args_m)) / (2 * step))
+                num[idx] = (4 * vals[0] - vals[1]) / 3
+            err = np.max(np.abs(num - grad))
+            assert err < 1e-9, f"d{name} differs from finite differences of the forward by {err}"
+
+
+def pin_bwd_torch_autograd(att, bwd):
+    """fp64 torch autograd through scaled_dot_product_attention (a library
+    routine), grouped heads by repeating K/V (autograd sums the copies), the
+    bottom-right causal mask given explicitly."""
+    import torch
+    import torch.nn.functional as F
+    for seed, (B, Hq, Hkv, Nq, Nk, d), causal in [
+        (81, (2, 4, 2, 33, 33, 16), True), (82, (1, 4, 1, 7, 40, 32), True), (83, (1, 2, 2, 20, 9, 8), False),
+        (84, (1, 2, 1, 1, 65, 64), True),
+    ]:
+        q, k, v = rand((B, Nq, Hq, d), seed), rand((B, Nk, Hkv, d), seed + 1), rand((B, Nk, Hkv, d), seed + 2)
+        do = rand((B, Nq, Hq, d), seed + 3)
+        sc = float(np.float32(1 / math.sqrt(d)))
+        dq, dk, dv = _full_bwd(bwd, q, k, v, do, sc, causal)
+        g = Hq // Hkv
+        tq = torch.from_numpy(q).double().permute(0, 2, 1, 3).requires_grad_()
+        tk = torch.from_numpy(k).double().permute(0, 2, 1, 3).requires_grad_()
+        tv = torch.from_numpy(v).double().permute(0, 2, 1, 3).requires_grad_()
+        keep = torch.ones(Nq, Nk, dtype=torch.bool).tril(Nk - Nq) if causal else None
+        out = F.scaled_dot_product_attention(tq, tk.repeat_interleave(g, dim=1), tv.repeat_interleave(g, dim=1),
+                                             attn_mask=keep, scale=sc)
+        out.backward(torch.from_numpy(do).double().permute(0, 2, 1, 3))
+        for name, mine, ref in (("dq", dq, tq.grad), ("dk", dk, tk.grad), ("dv", dv, tv.grad)):
+            err = float(np.max(np.abs(mine - ref.numpy())))
+            assert err < 1e-12, f"{name} differs from torch autograd by {err}"
+
+
+def pin_bwd_closed_forms(att, bwd):
+    # a single key: P = 1 for every row, so dq = dk = 0 and dv = sum of dO
+    # over the rows and the query heads of the group
+    q, k, v = rand((2, 9, 4, 8), 91), rand((2, 1, 2, 8), 92), rand((2, 1, 2, 8), 93)
+    do = rand((2, 9, 4, 8), 94)
+    for causal in (False, True):
+        dq, dk, dv = _full_bwd(bwd, q, k, v, do, 0.7, causal)
+        nvis_rows = 1 if causal else 9        # causal, Nk = 1: only the last query row sees the key
+        assert np.max(np.abs(dq)) < 1e-15 and np.max(np.abs(dk)) < 1e-15, "one key: dq and dk must vanish"
+        for b in range(2):
+            for hk in range(2):
+                want = do[b, 9 - nvis_rows:, 2 * hk:2 * hk + 2].astype(np.float64).sum(axis=(0, 1))
+                assert np.allclose(dv[b, hk, 0], want, atol=1e-13, rtol=0), "one key: dv = sum of dO"
+    # scale 0: uniform weights over the visible keys; dq = dk = 0 and
+    # dv_j = sum over the rows i that see j of dO_i / |visible keys of i|
+    N = 6
+    q, k, v, do = rand((1, N, 1, 4), 95), rand((1, N, 1, 4), 96), rand((1, N, 1, 4), 97), rand((1, N, 1, 4), 98)
+    dq, dk, dv = _full_bwd(bwd, q, k, v, do, 0.0, True)
+    assert np.max(np.abs(dq)) == 0 and np.max(np.abs(dk)) == 0
+    for j in range(N):
+        want = sum(do[0, i, 0].astype(np.float64) / (i + 1) for i in range(j, N))
+        assert np.allclose(dv[0, 0, j], want, atol=1e-14, rtol=0), "scale 0: dv"
+    # invariants on random inputs: sum_j dk_j = 0 (a common shift of every
+    # key moves each row's scores by a constant), sum_j dv_j = sum of dO over
+    # rows that see a key, and linearity in dO
+    B, Hq, Hkv, Nq, Nk, d = 1, 4, 2, 11, 8, 8
+    q, k, v = rand((B, Nq, Hq, d), 101, 2.0), rand((B, Nk, Hkv, d), 102), rand((B, Nk, Hkv, d), 103)
+    do1, do2 = rand((B, Nq, Hq, d), 104), rand((B, Nq, Hq, d), 105)
+    for causal in (False, True):
+        g1 = _full_bwd(bwd, q, k, v, do1, 0.5, causal)
+        g2 = _full_bwd(bwd, q, k, v, do2, 0.5, causal)
+        g12 = _full_bwd(bwd, q, k, v, (do1.astype(np.float64) + do2).astype(np.float32), 0.5, causal)
+        assert np.max(np.abs(g1[1].sum(axis=2))) < 1e-13, "sum over keys of dk must vanish"
+        first = max(0, Nq - Nk) if causal else 0            # rows before this see no key
+        for hk in range(Hkv):
+            want = do1[0, first:, 2 * hk:2 * hk + 2].astype(np.float64).sum(axis=(0, 1))
+            assert np.allclose(g1[2][0, hk].sum(axis=0), want, atol=1e-13, rtol=0), "sum over keys of dv"
+        s12 = (do1.astype(np.float64) + do2).astype(np.float32)
+        if np.array_equal(s12.astype(np.float64), do1.astype(np.float64) + do2):   # exact sum only
+            for a, b_, c in zip(g1, g2, g12):
+                assert np.max(np.abs(a + b_ - c)) < 1e-12, "gradients must be linear in dO"
+
+
+BWD_PINS = [pin_bwd_closed_forms, pin_bwd_torch_autograd, pin_bwd_finite_differences]

@@ -26,11 +26,21 @@ MUTATIONS = [
      "for (int x = 0; x < d; ++x) o_out[x] = 1.0;\n        *lse_out = 0.0;"),
     ("lse_dropped_max", "*lse_out = m + log(l);", "*lse_out = log(l);"),
     ("exp_sign", "l += exp(s[j] - m);", "l += exp(m - s[j]);"),
-    ("v_for_k", "const float *kj = J->k +", "const float *kj = J->v +"),
+    ("v_for_k", "const float *kj = J->k + (((int64_t)b * J->Nk + j)", "const float *kj = J->v + (((int64_t)b * J->Nk + j)"),
     ("v_reversed_coord", "o_out[x] += a * (double)vj[x];", "o_out[x] += a * (double)vj[d - 1 - x];"),
     ("q_from_key_row", "const float *qi = J->q + (((int64_t)b * J->Nq + i)", "const float *qi = J->q + (((int64_t)b * J->Nq + 0)"),
     ("no_normalise", "const double a = exp(s[j] - m) / l;", "const double a = exp(s[j] - m);"),
     ("max_not_subtracted_in_weights", "const double a = exp(s[j] - m) / l;", "const double a = exp(s[j]) / l;"),
+    # backward
+    ("bwd_no_softmax_jacobian", "const double ds = p[j] * (dp[j] - pdp);", "const double ds = p[j] * dp[j];"),
+    ("bwd_dk_sign", "dkj[x] += J->scale * ds * (double)qi[x];", "dkj[x] -= J->scale * ds * (double)qi[x];"),
+    ("bwd_dq_no_scale", "dqi[x] += J->scale * ds * (double)kj[x];", "dqi[x] += ds * (double)kj[x];"),
+    ("bwd_dv_unnormalised", "p[j] /= l;", "p[j] /= 1.0;"),
+    ("bwd_interleaved_groups", "const int h = J->hk * g + hh;", "const int h = J->hk + hh * J->Hkv;"),
+    ("bwd_causal_top_left", "const int64_t last = (int64_t)i + (Nk - Nq);", "const int64_t last = (int64_t)i;"),
+    ("bwd_dp_uses_k", "t += (double)doi[x] * (double)vj[x];", "t += (double)doi[x] * (double)kj[x];"),
+    ("bwd_last_thread_sum_dropped", "for (int t = 0; t < nthreads; ++t) {\n                sk +=",
+     "for (int t = 1; t < nthreads; ++t) {\n                sk +="),
 ]
 
 
@@ -52,10 +62,17 @@ def test_planted_mistake_is_caught(name, tmp_path_factory):
     so = _build(name, str(tmp_path_factory.mktemp("mut")))
     lib = oracle._open(so)
     att = functools.partial(oracle.attention, _lib_override=lib)
+    bwd = functools.partial(oracle.attention_bwd, _lib_override=lib)
     failed = []
     for pin in pins.ALL_PINS:
         try:
             pin(att)
         except (AssertionError, RuntimeError, FloatingPointError, ValueError):
             failed.append(pin.__name__)
+    if name.startswith("bwd_"):
+        for pin in pins.BWD_PINS:
+            try:
+                pin(att, bwd)
+            except (AssertionError, RuntimeError, FloatingPointError, ValueError):
+                failed.append(pin.__name__)
     assert failed, f"no pin caught the planted mistake {name}"
