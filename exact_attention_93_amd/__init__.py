@@ -15,6 +15,11 @@ log-sum-exp of each row's scaled, masked scores.  Equal lengths and one key
 range go to fa_fwd / fa_fwd_f32; unequal lengths (bottom-right causal
 alignment) or a split key sequence go to fa_fwd_splitkv(_f32), with the
 workspace allocated here by torch.
+
+    dq, dk, dv = bwd(q, k, v, o, lse, dout, causal=False, scale=None)
+
+Gradients through fa_bwd (bf16): o and lse are the forward's outputs for
+the same q, k, v, causal and scale; dout has o's shape.
 """
 from __future__ import annotations
 
@@ -24,7 +29,7 @@ import os
 
 from ._build import LIB_PATH
 
-__all__ = ["fwd", "fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_splitkv_num_splits",
+__all__ = ["fwd", "bwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_splitkv_num_splits",
            "fa_splitkv_workspace_size", "fa_strerror", "fa_version", "load_library", "FAError",
            "STATUS", "EXPORTS"]
 
@@ -34,7 +39,7 @@ STATUS = {
     "FA_ERR_SPLITS": 9, "FA_ERR_WORKSPACE": 10,
 }
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_splitkv_num_splits",
-           "fa_splitkv_workspace_size", "fa_strerror", "fa_version")
+           "fa_splitkv_workspace_size", "fa_bwd", "fa_bwd_workspace_size", "fa_strerror", "fa_version")
 
 _lib = None
 
@@ -70,6 +75,11 @@ def load_library(path: str = LIB_PATH):
     lib.fa_splitkv_num_splits.argtypes = [ctypes.c_int] * 7
     lib.fa_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.fa_splitkv_workspace_size.argtypes = [ctypes.c_int] * 7
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 9 + [ctypes.c_int] * 6 + [ctypes.c_float, ctypes.c_int,
+                           ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
+    lib.fa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.fa_bwd_workspace_size.argtypes = [ctypes.c_int] * 3
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_strerror.argtypes = [ctypes.c_int]
     lib.fa_version.restype = ctypes.c_int
@@ -163,3 +173,47 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
     if st != 0:
         raise FAError(st, fa_strerror(st))
     return out, lse
+
+
+def fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale, causal, ws, ws_bytes, stream) -> int:
+    return load_library().fa_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, float(scale),
+                                 int(causal), ws, ws_bytes, stream)
+
+
+def fa_bwd_workspace_size(B, Hq, Nq) -> int:
+    return load_library().fa_bwd_workspace_size(B, Hq, Nq)
+
+
+def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, dq=None, dk=None, dv=None,
+        workspace=None, stream=None):
+    """Attention backward through libfa.so (bf16).  Returns (dq, dk, dv)."""
+    import torch
+
+    ts = (q, k, v, o, dout)
+    if not all(t.is_cuda for t in ts) or not lse.is_cuda:
+        raise ValueError("bwd: every tensor must be on the GPU (there is no CPU path)")
+    if any(t.dtype != torch.bfloat16 for t in ts) or lse.dtype != torch.float32:
+        raise ValueError("bwd: q, k, v, o, dout must be bfloat16 and lse float32")
+    if not all(t.is_contiguous() for t in ts) or not lse.is_contiguous():
+        raise ValueError("bwd: tensors must be contiguous")
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if (tuple(k.shape) != (B, Nk, Hkv, d) or v.shape != k.shape or o.shape != q.shape or dout.shape != q.shape
+            or tuple(lse.shape) != (B, Hq, Nq)):
+        raise ValueError("bwd: shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = fa_bwd_workspace_size(B, Hq, Nq)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    if st != 0:
+        raise FAError(st, fa_strerror(st))
+    return dq, dk, dv

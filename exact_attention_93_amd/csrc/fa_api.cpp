@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 101;  // 0.1.1
+constexpr int kVersion = 102;  // 0.1.2
 constexpr int kMaxSplits = 256;
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb)
@@ -209,6 +209,68 @@ size_t fa_splitkv_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, 
     return workspace_bytes_for(B, Hq, Nq, d, nsplit);
 }
 
+size_t fa_bwd_workspace_size(int B, int Hq, int Nq)
+{
+    if (B < 1 || Hq < 1 || Nq < 1) return 0;
+    return (size_t)B * Hq * Nq * sizeof(float);
+}
+
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+           const void *dout, void *dq, void *dk, void *dv, int B, int Hq, int Hkv, int Nq, int Nk,
+           int d, float scale, int causal, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+    if (Hq % Hkv != 0) return FA_ERR_HEADS;
+    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (((int64_t)Nq + 256) * Hq * d >= ((int64_t)1 << 29)) return FA_ERR_SHAPE;
+    if (((int64_t)Nk + 256) * Hkv * d >= ((int64_t)1 << 29)) return FA_ERR_SHAPE;
+    if ((int64_t)B * Hq * cdiv(Nq, 128) >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+    if ((int64_t)B * Hkv * cdiv(Nk, 128) >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
+         (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15)
+        return FA_ERR_ALIGN;
+    if (((uintptr_t)lse | (uintptr_t)workspace) & 3) return FA_ERR_ALIGN;
+    if (!isfinite(scale)) return FA_ERR_SCALE;
+    const size_t need = fa_bwd_workspace_size(B, Hq, Nq);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    const size_t nq = (size_t)B * Nq * Hq * d * 2, nk = (size_t)B * Nk * Hkv * d * 2;
+    const size_t nl = (size_t)B * Hq * Nq * sizeof(float);
+    const void *ins[6] = {q, k, v, o, dout, lse};
+    const size_t insz[6] = {nq, nk, nk, nq, nq, nl};
+    void *outs[4] = {dq, dk, dv, workspace};
+    const size_t outsz[4] = {nq, nk, nk, need};
+    for (int a = 0; a < 4; ++a) {
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(outs[a], outsz[a], ins[i], insz[i])) return FA_ERR_ALIAS;
+        for (int c2 = a + 1; c2 < 4; ++c2)
+            if (overlaps(outs[a], outsz[a], outs[c2], outsz[c2])) return FA_ERR_ALIAS;
+    }
+
+    fa::BwdParams p;
+    p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
+    p.delta = (float *)workspace;
+    p.dq = dq; p.dk = dk; p.dv = dv;
+    p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk;
+    p.off = Nk - Nq;
+    p.group = Hq / Hkv;
+    p.causal = causal ? 1 : 0;
+    p.xcd_groups = ((B * Hkv) % 8 == 0) ? 1 : 0;
+    p.scale = scale;
+    if (scale > 0.f) {
+        p.qmode = 0;
+        p.c = (float)((double)scale * 1.4426950408889634);
+    } else if (scale < 0.f) {
+        p.qmode = 1;
+        p.c = (float)(-(double)scale * 1.4426950408889634);
+    } else {
+        p.qmode = 2;
+        p.c = 1.f;
+    }
+    if (!(p.c >= FLT_MIN) || !isfinite(p.c)) return FA_ERR_SCALE;
+    return fa::launch_bwd_bf16(p, d, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 const char *fa_strerror(int status)
 {
     switch (status) {
@@ -222,7 +284,7 @@ const char *fa_strerror(int status)
     case FA_ERR_ALIAS: return "an output or the workspace overlaps an input or another output";
     case FA_ERR_LAUNCH: return "the HIP runtime reported an error for the kernel launch";
     case FA_ERR_SPLITS: return "num_splits must be in 0..256";
-    case FA_ERR_WORKSPACE: return "workspace missing, smaller than fa_splitkv_workspace_size, or not 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "workspace missing or smaller than the size function returns (split forward: also 16-byte aligned)";
     default: return "unknown fa_status";
     }
 }

@@ -1,0 +1,519 @@
+// Attention backward, bf16 in / bf16 out, fp32 accumulation, on CDNA4
+// (gfx950) matrix cores.
+//
+// Gradients of O = softmax(scale Q K^T [+ causal mask]) V for an upstream
+// gradient dO, with P recomputed from the row log-sum-exp the forward
+// stored, never read from memory ("[Attention优化] 从Online-Softmax到
+// FlashAttention V1/V2/V3", sections 0x04 and 0x05; "FlashAttention：IO 感知的
+// 精确注意力", section 6):
+//     P = exp(scale Q K^T - lse),  dP = dO V^T,  delta_i = sum_x dO_ix O_ix,
+//     dS = P o (dP - delta),  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
+// (delta_i equals sum_j P_ij dP_ij, the softmax Jacobian term, because
+// O_i = sum_j P_ij v_j.)
+//
+// Two kernels.  The first is Q-outer like the forward: a workgroup owns 128
+// query rows of one head, computes delta for them (stored for the second
+// kernel) and streams the visible K/V tiles, accumulating dQ in registers.
+// The second is K/V-outer, the loop order the first page gives for the
+// FlashAttention-2 backward: a workgroup owns 128 keys of one K/V head,
+// holds K and V in registers and streams the query tiles (of every query
+// head of the group, so grouped-query attention needs no reduction across
+// workgroups), accumulating dK and dV in registers.  The pages accumulate dQ
+// across the K/V-outer workgroups with atomic additions instead; here dQ
+// gets its own pass, which costs one more score product per tile but keeps
+// the result deterministic and avoids a float atomic per dQ element for
+// every (query tile, key tile) pair.
+//
+// Matrix-core layout (v_mfma_f32_32x32x16_bf16): as in the forward, each
+// product is arranged so that one operand comes from registers and the
+// other from LDS, and the accumulator of one product feeds the next as its
+// B operand: first kernel S^T = K Q^T, dP^T = V dO^T (lane = query) and
+// dQ^T += K^T dS^T; second kernel S = Q K^T, dP = dO V^T (lane = key),
+// dV^T += dO^T P and dK^T += Q^T dS.  The rows of the LDS operand of the
+// first two products are taken in the order that swaps bits 2 and 3 of the
+// row index, so that accumulator register i of lane half hf holds row
+// 16*(i/8) + 8*hf + (i%8), the K-slot order of the next product's B operand.
+// Transposed operands are read with ds_read_b64_tr_b16.  LDS tiles are read
+// both ways, so their 16-byte chunks are permuted by one XOR that is
+// conflict-free for 16-byte row reads and for the transpose reads.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x16_t mfma_bf16(u32x4_t a, u32x4_t b, f32x16_t c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
+{
+    f32x2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+__device__ __forceinline__ float dot_bf16x2(uint32_t a, uint32_t b, float acc)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+__device__ __forceinline__ float sum_halves(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Chunk permutation of every LDS tile here: conflict-free for a 16-byte
+// operand read of 16 consecutive rows and for one transpose-read phase
+// (4 consecutive rows x 4 consecutive chunks).
+template <int D> __device__ __forceinline__ int swz(int row)
+{
+    return D == 128 ? (4 * (row & 3) | ((row >> 2) & 3)) : (4 * ((row >> 1) & 1) | ((row >> 2) & 3));
+}
+
+__device__ __forceinline__ void load_lds16(const void *base, int range, uint32_t off, lds_void_t *dst)
+{
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, range, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(const void *base, int range, uint32_t off, lds_void_t *dst)
+{
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, range, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, off, 0, 0, 0);
+}
+
+__device__ __forceinline__ void vm_wait_all()
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// A rows of the first two products: bits 2 and 3 of the lane's row swapped.
+__device__ __forceinline__ int perm_row(int l) { return (l & 0x13) | ((l & 4) << 1) | ((l & 8) >> 1); }
+
+// Transposed operand from an LDS tile [rows][D] (bf16, chunks permuted by swz):
+// lane i of each 16-lane group gets rows r0 + 16u + 8*(i/16 & 2)/2 ... as laid
+// out for the A operand of a 32x32x16 product: A[x][k] = tile[16u + k][32xb + x].
+template <int D>
+__device__ __forceinline__ u32x4_t tr_operand(const char *tile, int u, int xb, int lane)
+{
+    const int tg = lane >> 4, ts = lane & 15;
+    const int tr_row = 8 * (tg >> 1) + (ts >> 2);
+    const int tr_chunk = 2 * (tg & 1) + ((ts & 3) >> 1);
+    const int tr_byte = 8 * (ts & 1);
+    u32x4_t a;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int row = 16 * u + 4 * r + tr_row;
+        const int off = row * (D * 2) + (((4 * xb + tr_chunk) ^ swz<D>(row)) * 16) + tr_byte;
+        const i16x4_t t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(tile + off));
+        const u32x2_t t2 = __builtin_bit_cast(u32x2_t, t4);
+        a[2 * r] = t2[0];
+        a[2 * r + 1] = t2[1];
+    }
+    return a;
+}
+
+// 16 bytes of row `row`, logical chunk `ch`, of an LDS tile.
+template <int D>
+__device__ __forceinline__ u32x4_t row_chunk(const char *tile, int row, int ch)
+{
+    return *(const u32x4_t *)(tile + row * (D * 2) + ((ch ^ swz<D>(row)) * 16));
+}
+
+// ============================================================ dQ (Q-outer)
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p)
+{
+    constexpr int BM = 128, BN = 64;
+    constexpr int KSTEPS = D / 16, XB = D / 32, NKB = BN / 32;
+    constexpr int CHUNKS = D / 8, ROW_BYTES = D * 2, ROWS_PER_BLK = 1024 / ROW_BYTES;
+    constexpr int BLKS = BN * ROW_BYTES / 1024, BLKS_PER_WAVE = BLKS / 4;
+    constexpr int TILE = BN * D;
+
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs1[TILE];
+
+    // (batch, head, query tile): heaviest causal tiles first
+    const int L = blockIdx.x;
+    const int per = p.B * p.Hq;
+    const int t_ord = L / per;
+    const int bh = L - t_ord * per;
+    const int b = bh / p.Hq, h = bh - (bh / p.Hq) * p.Hq;
+    const int ntq = (p.Nq + BM - 1) / BM;
+    const int tile = CAUSAL ? ntq - 1 - t_ord : t_ord;
+    const int hk = h / p.group;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lq = lane & 31, hf = lane >> 5;
+    const int Nq = p.Nq, Nk = p.Nk, off = p.off;
+    const int q_first = tile * BM, wq0 = q_first + wave * 32, my_q = wq0 + lq;
+    const float c = p.c;
+    const int sK = p.Hkv * D;
+
+    // ---- this lane's query row: Q^T and dO^T operands, delta, lse (base 2)
+    u32x4_t qreg[KSTEPS], doreg[KSTEPS];
+    float delta = 0.f, lse2 = INFINITY;        // +inf: P = 0 for rows without keys and past the end
+    if (my_q < Nq) {
+        const int64_t rowoff = (((int64_t)b * Nq + my_q) * p.Hq + h) * D;
+        const u32x4_t *qs = (const u32x4_t *)((const uint16_t *)p.q + rowoff);
+        const u32x4_t *ds = (const u32x4_t *)((const uint16_t *)p.dout + rowoff);
+        const u32x4_t *os = (const u32x4_t *)((const uint16_t *)p.o + rowoff);
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+            qreg[t] = qs[2 * t + hf];
+            doreg[t] = ds[2 * t + hf];
+            const u32x4_t ov = os[2 * t + hf];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) delta = dot_bf16x2(doreg[t][e], ov[e], delta);
+        }
+        const float l = p.lse[((int64_t)b * p.Hq + h) * Nq + my_q];
+        lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
+    } else {
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) qreg[t] = doreg[t] = u32x4_t{0, 0, 0, 0};
+    }
+    delta = sum_halves(delta);
+    if (hf == 0 && my_q < Nq) p.delta[((int64_t)b * p.Hq + h) * Nq + my_q] = delta;
+    if (p.qmode != 0) {
+        const uint32_t keep = p.qmode == 2 ? 0u : 0xffffffffu;
+        const uint32_t flip = p.qmode == 1 ? 0x80008000u : 0u;
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) qreg[t][e] = (qreg[t][e] ^ flip) & keep;
+    }
+
+    // ---- key tiles: all of them, or (causal) up to the last one the tile's last row sees
+    int n = (Nk + BN - 1) / BN;
+    if (CAUSAL) {
+        const int last = min(q_first + BM, Nq) - 1 + off;
+        n = last < 0 ? 0 : min(n, last / BN + 1);
+    }
+    const bool wave_live = wq0 < Nq;
+    auto visible = [&](int j) { return wave_live && (!CAUSAL || j * BN <= wq0 + 31 + off); };
+
+    const uint16_t *kbase = (const uint16_t *)p.k + ((int64_t)b * Nk * p.Hkv + hk) * D;
+    const uint16_t *vbase = (const uint16_t *)p.v + ((int64_t)b * Nk * p.Hkv + hk) * D;
+    const int range = Nk * sK * 2;
+    const int ld_row = lane / CHUNKS, ld_pch = lane % CHUNKS;
+    auto load = [&](int j, uint16_t *kd, uint16_t *vd) {
+#pragma unroll
+        for (int i = 0; i < BLKS_PER_WAVE; ++i) {
+            const int blk = wave * BLKS_PER_WAVE + i;
+            const int row = blk * ROWS_PER_BLK + ld_row;
+            const uint32_t o = (uint32_t)(j * BN + row) * (uint32_t)(sK * 2) + ((ld_pch ^ swz<D>(row)) * 16);
+            load_lds16(kbase, range, o, (lds_void_t *)&kd[blk * 512]);
+            load_lds16(vbase, range, o, (lds_void_t *)&vd[blk * 512]);
+        }
+    };
+
+    f32x16_t dqacc[XB];
+#pragma unroll
+    for (int xb = 0; xb < XB; ++xb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dqacc[xb][i] = 0.f;
+    const int prow = perm_row(lq);
+
+    // One 32-key half of the tile at a time: S^T and dP^T for those keys,
+    // dS^T in bf16, then its share of dQ^T += K^T dS^T.
+    auto compute = [&](int j, const uint16_t *ks_, const uint16_t *vs_) {
+        const char *ks = (const char *)ks_, *vs = (const char *)vs_;
+        const int key0 = j * BN;
+        const bool need_mask = (key0 + BN > Nk) || (CAUSAL && key0 + BN - 1 > wq0 + off);
+        const int lim = (CAUSAL ? min(my_q + off, Nk - 1) : Nk - 1) - (key0 + 8 * hf);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            f32x16_t s, dp;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+            const int row = kb * 32 + prow;
+#pragma unroll
+            for (int t = 0; t < KSTEPS; ++t) {
+                s = mfma_bf16(row_chunk<D>(ks, row, 2 * t + hf), qreg[t], s);
+                dp = mfma_bf16(row_chunk<D>(vs, row, 2 * t + hf), doreg[t], dp);
+            }
+            u32x4_t dsb[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    float e2[2];
+#pragma unroll
+                    for (int z = 0; z < 2; ++z) {
+                        const int i = 8 * u + 2 * w + z;
+                        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lse2));
+                        if (need_mask && kb * 32 + 16 * u + 2 * w + z > lim) pv = 0.f;
+                        e2[z] = pv * (dp[i] - delta);
+                    }
+                    dsb[u][w] = pack_bf16(e2[0], e2[1]);
+                }
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int xb = 0; xb < XB; ++xb)
+                    dqacc[xb] = mfma_bf16(tr_operand<D>(ks, 2 * kb + u, xb, lane), dsb[u], dqacc[xb]);
+        }
+    };
+
+    if (n > 0) load(0, Ks0, Vs0);
+    for (int j = 0; j < n; j += 2) {
+        vm_wait_all();
+        __syncthreads();                  // tile j resident; every wavefront is done with tile j-1
+        if (j + 1 < n) load(j + 1, Ks1, Vs1);
+        if (visible(j)) compute(j, Ks0, Vs0);
+        if (j + 1 < n) {
+            vm_wait_all();
+            __syncthreads();
+            if (j + 2 < n) load(j + 2, Ks0, Vs0);
+            if (visible(j + 1)) compute(j + 1, Ks1, Vs1);
+        }
+    }
+
+    if (my_q < Nq) {
+        uint16_t *dst = (uint16_t *)p.dq + (((int64_t)b * Nq + my_q) * p.Hq + h) * D;
+        const float sc = p.scale;
+#pragma unroll
+        for (int xb = 0; xb < XB; ++xb)
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                const int x = xb * 32 + 8 * gi + 4 * hf;
+                const u32x2_t w = {pack_bf16(dqacc[xb][4 * gi] * sc, dqacc[xb][4 * gi + 1] * sc),
+                                   pack_bf16(dqacc[xb][4 * gi + 2] * sc, dqacc[xb][4 * gi + 3] * sc)};
+                *(u32x2_t *)(dst + x) = w;
+            }
+    }
+}
+
+// ====================================================== dK, dV (K/V-outer)
+template <int D, bool CAUSAL>
+__global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p)
+{
+    constexpr int BN = 128, BQ = 64;     // keys per workgroup, query rows per tile
+    constexpr int KSTEPS = D / 16, XB = D / 32, NQB = BQ / 32;
+    constexpr int CHUNKS = D / 8, ROW_BYTES = D * 2, ROWS_PER_BLK = 1024 / ROW_BYTES;
+    constexpr int BLKS = BQ * ROW_BYTES / 1024, BLKS_PER_WAVE = BLKS / 4;
+    constexpr int TILE = BQ * D;
+
+    __shared__ __attribute__((aligned(1024))) uint16_t Qs0[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Qs1[TILE];
+    __shared__ __attribute__((aligned(1024))) uint16_t Os0[TILE];   // dO
+    __shared__ __attribute__((aligned(1024))) uint16_t Os1[TILE];
+    __shared__ __attribute__((aligned(16))) float Ls0[BQ], Ls1[BQ], Ds0[BQ], Ds1[BQ];
+
+    // (batch, K/V head, key tile); with B*Hkv a multiple of 8, every key tile
+    // of a head runs on one XCD, whose L2 then serves that head's Q and dO
+    const int L = blockIdx.x;
+    int b, hk, kt;
+    if (p.xcd_groups) {
+        const int xcd = L & 7, s = L >> 3;
+        const int heads_here = (p.B * p.Hkv) >> 3;
+        kt = s / heads_here;
+        const int g = (s - kt * heads_here) * 8 + xcd;
+        b = g / p.Hkv;
+        hk = g - b * p.Hkv;
+    } else {
+        const int per = p.B * p.Hkv;
+        kt = L / per;
+        const int r = L - kt * per;
+        b = r / p.Hkv;
+        hk = r - b * p.Hkv;
+    }
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lk = lane & 31, hf = lane >> 5;
+    const int Nq = p.Nq, Nk = p.Nk, off = p.off, G = p.group;
+    const int k_first = kt * BN, wk0 = k_first + wave * 32, my_k = wk0 + lk;
+    const float c = p.c;
+    const int sQ = p.Hq * D;
+
+    // ---- this lane's key: K and V rows as B operands (K sign/zero as the scale needs)
+    u32x4_t kreg[KSTEPS], vreg[KSTEPS];
+    if (my_k < Nk) {
+        const int64_t rowoff = (((int64_t)b * Nk + my_k) * p.Hkv + hk) * D;
+        const u32x4_t *ks = (const u32x4_t *)((const uint16_t *)p.k + rowoff);
+        const u32x4_t *vs = (const u32x4_t *)((const uint16_t *)p.v + rowoff);
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+            kreg[t] = ks[2 * t + hf];
+            vreg[t] = vs[2 * t + hf];
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) kreg[t] = vreg[t] = u32x4_t{0, 0, 0, 0};
+    }
+    if (p.qmode != 0) {
+        const uint32_t keep = p.qmode == 2 ? 0u : 0xffffffffu;
+        const uint32_t flip = p.qmode == 1 ? 0x80008000u : 0u;
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) kreg[t][e] = (kreg[t][e] ^ flip) & keep;
+    }
+
+    // ---- query tiles: causal rows i see key j iff i >= j - off
+    const int q_lo = CAUSAL ? max(0, k_first - off) : 0;
+    const int qt_lo = q_lo / BQ;
+    const int nqt = q_lo < Nq ? (Nq + BQ - 1) / BQ - qt_lo : 0;
+    const int total = G * nqt;            // (query head in group, query tile) pairs
+    const bool wave_live = wk0 < Nk;
+
+    const int range = Nq * sQ * 2;
+    const int ld_row = lane / CHUNKS, ld_pch = lane % CHUNKS;
+    auto load = [&](int it, uint16_t *qd, uint16_t *od, float *ld, float *dd) {
+        const int hh = it / nqt, qt = qt_lo + (it - (it / nqt) * nqt);
+        const int h = hk * G + hh;
+        const uint16_t *qb = (const uint16_t *)p.q + ((int64_t)b * Nq * p.Hq + h) * D;
+        const uint16_t *ob = (const uint16_t *)p.dout + ((int64_t)b * Nq * p.Hq + h) * D;
+#pragma unroll
+        for (int i = 0; i < BLKS_PER_WAVE; ++i) {
+            const int blk = wave * BLKS_PER_WAVE + i;
+            const int row = blk * ROWS_PER_BLK + ld_row;
+            const uint32_t o = (uint32_t)(qt * BQ + row) * (uint32_t)(sQ * 2) + ((ld_pch ^ swz<D>(row)) * 16);
+            load_lds16(qb, range, o, (lds_void_t *)&qd[blk * 512]);
+            load_lds16(ob, range, o, (lds_void_t *)&od[blk * 512]);
+        }
+        if (wave == 0) {                  // the tile's 64 lse and delta values
+            const int64_t r0 = ((int64_t)b * p.Hq + h) * Nq;
+            const int rng = max(0, Nq - qt * BQ) * 4;
+            load_lds4(p.lse + r0 + qt * BQ, rng, lane * 4, (lds_void_t *)ld);
+            load_lds4(p.delta + r0 + qt * BQ, rng, lane * 4, (lds_void_t *)dd);
+        }
+    };
+
+    f32x16_t dk[XB], dv[XB];
+#pragma unroll
+    for (int xb = 0; xb < XB; ++xb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dk[xb][i] = dv[xb][i] = 0.f;
+    const int prow = perm_row(lk);
+
+    auto compute = [&](int it, const uint16_t *qs_, const uint16_t *os_, const float *ls, const float *dsm) {
+        const int qt = qt_lo + (it - (it / nqt) * nqt);
+        const char *qs = (const char *)qs_, *os = (const char *)os_;
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+            const int qrow0 = qt * BQ + qb * 32;           // first query row of this block
+            if (CAUSAL && qrow0 + 31 + off < wk0) continue; // no row of the block sees a key of this wavefront
+            f32x16_t s, dp;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+            const int row = qb * 32 + prow;
+#pragma unroll
+            for (int t = 0; t < KSTEPS; ++t) {
+                s = mfma_bf16(row_chunk<D>(qs, row, 2 * t + hf), kreg[t], s);
+                dp = mfma_bf16(row_chunk<D>(os, row, 2 * t + hf), vreg[t], dp);
+            }
+            // register i holds query row qrow0 + 16*(i/8) + 8*hf + (i%8)
+            const bool need_mask = (qrow0 + 32 > Nq) || (CAUSAL && qrow0 + off < wk0 + 31);
+            u32x4_t pb[2], dsb[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int lq0 = qb * 32 + 16 * u + 8 * hf;   // first of the 8 rows in LDS order
+                const f32x4_t la = *(const f32x4_t *)&ls[lq0], lb = *(const f32x4_t *)&ls[lq0 + 4];
+                const f32x4_t da = *(const f32x4_t *)&dsm[lq0], db = *(const f32x4_t *)&dsm[lq0 + 4];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    float pv[2], dsv[2];
+#pragma unroll
+                    for (int z = 0; z < 2; ++z) {
+                        const int e = 2 * w + z, i = 8 * u + e;
+                        const float lr = e < 4 ? la[e] : lb[e - 4];
+                        const float dr = e < 4 ? da[e] : db[e - 4];
+                        const float l2 = lr == -INFINITY ? INFINITY : lr * kLog2e;
+                        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -l2));
+                        if (need_mask) {
+                            const int qi = qrow0 + 16 * u + 8 * hf + e;
+                            if (qi >= Nq || (CAUSAL && my_k > qi + off)) pe = 0.f;
+                        }
+                        pv[z] = pe;
+                        dsv[z] = pe * (dp[i] - dr);
+                    }
+                    pb[u][w] = pack_bf16(pv[0], pv[1]);
+                    dsb[u][w] = pack_bf16(dsv[0], dsv[1]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int xb = 0; xb < XB; ++xb) {
+                    dv[xb] = mfma_bf16(tr_operand<D>(os + qb * 32 * ROW_BYTES, u, xb, lane), pb[u], dv[xb]);
+                    dk[xb] = mfma_bf16(tr_operand<D>(qs + qb * 32 * ROW_BYTES, u, xb, lane), dsb[u], dk[xb]);
+                }
+        }
+    };
+
+    if (total > 0) load(0, Qs0, Os0, Ls0, Ds0);
+    for (int it = 0; it < total; it += 2) {
+        vm_wait_all();
+        __syncthreads();
+        if (it + 1 < total) load(it + 1, Qs1, Os1, Ls1, Ds1);
+        if (wave_live) compute(it, Qs0, Os0, Ls0, Ds0);
+        if (it + 1 < total) {
+            vm_wait_all();
+            __syncthreads();
+            if (it + 2 < total) load(it + 2, Qs0, Os0, Ls0, Ds0);
+            if (wave_live) compute(it + 1, Qs1, Os1, Ls1, Ds1);
+        }
+    }
+
+    if (my_k < Nk) {
+        const int64_t rowoff = (((int64_t)b * Nk + my_k) * p.Hkv + hk) * D;
+        uint16_t *dkd = (uint16_t *)p.dk + rowoff;
+        uint16_t *dvd = (uint16_t *)p.dv + rowoff;
+        const float sc = p.scale;
+#pragma unroll
+        for (int xb = 0; xb < XB; ++xb)
+#pragma unroll
+            for (int gi = 0; gi < 4; ++gi) {
+                const int x = xb * 32 + 8 * gi + 4 * hf;
+                const u32x2_t wk = {pack_bf16(dk[xb][4 * gi] * sc, dk[xb][4 * gi + 1] * sc),
+                                    pack_bf16(dk[xb][4 * gi + 2] * sc, dk[xb][4 * gi + 3] * sc)};
+                const u32x2_t wv = {pack_bf16(dv[xb][4 * gi], dv[xb][4 * gi + 1]),
+                                    pack_bf16(dv[xb][4 * gi + 2], dv[xb][4 * gi + 3])};
+                *(u32x2_t *)(dkd + x) = wk;
+                *(u32x2_t *)(dvd + x) = wv;
+            }
+    }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_one(const BwdParams &p, hipStream_t stream)
+{
+    const unsigned g1 = (unsigned)p.B * (unsigned)p.Hq * (unsigned)((p.Nq + 127) / 128);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(g1), dim3(kThreads), 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned g2 = (unsigned)p.B * (unsigned)p.Hkv * (unsigned)((p.Nk + 127) / 128);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(g2), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdParams &p, int d, hipStream_t stream)
+{
+    if (d == 128) return p.causal ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
+    return p.causal ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
+}
+
+}  // namespace fa

@@ -40,6 +40,22 @@ constexpr int kDecodeRowBlock = 32;
 constexpr int kDecodeMaxRows = 64;
 inline bool use_decode(int Nq, int group) { return (int64_t)Nq * group <= kDecodeMaxRows; }
 hipError_t launch_fwd_f32(const FwdParams &p, int d, hipStream_t stream);
+struct BwdParams {
+    const void *q, *k, *v, *o, *dout;   // bf16 inputs (o: the forward's output)
+    const float *lse;                   // the forward's log-sum-exp [B][Hq][Nq]
+    float *delta;                       // workspace: rowsum(dO * O) [B][Hq][Nq]
+    void *dq, *dk, *dv;                 // bf16 outputs
+    int B, Hq, Hkv, Nq, Nk;
+    int off;                            // Nk - Nq (bottom-right causal alignment)
+    int group;                          // Hq / Hkv
+    int causal;
+    int xcd_groups;                     // 1 when B*Hkv is a multiple of 8
+    int qmode;                          // as in FwdParams (q or k negated / zeroed for the scale's sign)
+    float c;                            // |scale| * log2(e), or 1 when scale == 0
+    float scale;                        // the signed scale (dq = scale dS K, dk = scale dS^T Q)
+};
+hipError_t launch_bwd_bf16(const BwdParams &p, int d, hipStream_t stream);
+
 // Merge of the nsplit partial results into o (bf16 when out_bf16, else fp32) and lse.
 hipError_t launch_combine(const FwdParams &p, int d, int out_bf16, hipStream_t stream);
 

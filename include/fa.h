@@ -144,6 +144,40 @@ int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num
  */
 size_t fa_splitkv_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
 
+/*
+ * fa_bwd -- gradients of the bf16 forward (fa_fwd / fa_fwd_splitkv) for an
+ * upstream gradient dout = dL/do.
+ *
+ *   dv = P^T dout,  dq = scale * dS k,  dk = scale * dS^T q,
+ *   dS = P o (dout v^T - delta),  delta_i = sum_x dout[i,x] * o[i,x],
+ * with P = exp(scale q k^T - lse) recomputed from the forward's lse (zero
+ * where masked) rather than stored: the backward of the first page's
+ * sections 0x04 and 0x05 and of the second page's section 6
+ * ("FlashAttention：IO 感知的精确注意力").  For grouped-query attention dk and
+ * dv of a key/value head are summed over the query heads that read it.
+ *   q, o, dout, dq : bf16 [B][Nq][Hq][d];   k, v, dk, dv : bf16 [B][Nk][Hkv][d];
+ *   lse            : fp32 [B][Hq][Nq], as fa_fwd wrote it (rows without keys
+ *                    hold -inf and get zero gradients);
+ *   o              : the forward's output for the same q, k, v, scale, causal;
+ *   scale, causal  : as passed to the forward;
+ *   workspace      : at least fa_bwd_workspace_size(B, Hq, Nq) bytes of device
+ *                    memory, 4-byte aligned, owned by the caller; overwritten
+ *                    (it receives delta).
+ * dq, dk, dv are fully written, rounded to nearest even.  Two kernels are
+ * enqueued on `stream`: dq (query-block outer, also writing delta) and then
+ * dk, dv (key-block outer).  The result is deterministic (no atomics).
+ * Errors and limits as for fa_fwd_splitkv, plus FA_ERR_WORKSPACE for a
+ * missing or short workspace; every output must be 16-byte aligned and
+ * overlap no input, no other output and not the workspace.
+ */
+int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
+           const void *dout, void *dq, void *dk, void *dv, int B, int Hq, int Hkv,
+           int Nq, int Nk, int d, float scale, int causal, void *workspace,
+           size_t workspace_bytes, void *stream);
+
+/* Workspace bytes fa_bwd needs: B * Hq * Nq * 4 (0 for invalid sizes). */
+size_t fa_bwd_workspace_size(int B, int Hq, int Nq);
+
 /* Human-readable text for an fa_status value (static storage, never NULL). */
 const char *fa_strerror(int status);
 

@@ -46,7 +46,7 @@ def test_status_codes_match_header():
 
 
 def test_version_and_strerror(lib):
-    assert fa.fa_version() == 101
+    assert fa.fa_version() == 102
     for st in range(11):
         assert fa.fa_strerror(st)
     assert "unknown" in fa.fa_strerror(99)
@@ -151,3 +151,32 @@ def test_split_shape_helpers(lib):
     assert n(1, 4, 2, 1, 100, 96, 0) == -fa.STATUS["FA_ERR_HEADDIM"]
     assert n(1, 4, 2, 1, 100, 64, -2) == -fa.STATUS["FA_ERR_SPLITS"]
     assert w(1, 3, 2, 1, 100, 64, 4) == 0
+
+
+def bcall(q=Q, k=K, v=V, o=O, lse=L, do=0x70000000, dq=0x80000000, dk=0x90000000, dv=0xA0000000,
+          ws=W, ws_bytes=1 << 24, **kw):
+    a = dict(B=2, Hq=4, Hkv=2, Nq=16, Nk=300, d=64, scale=0.125, causal=1)
+    a.update(kw)
+    return fa.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                     a["scale"], a["causal"], ws, ws_bytes, None)
+
+
+def test_invalid_arguments_bwd(lib):
+    S = fa.STATUS
+    for name in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv"):
+        assert bcall(**{name: None}) == S["FA_ERR_NULL"], name
+    for bad in (dict(B=0), dict(Nq=0), dict(Nk=0), dict(Hkv=0)):
+        assert bcall(**bad) == S["FA_ERR_SHAPE"], bad
+    assert bcall(Nk=1 << 20, Hkv=32, Hq=32, d=128) == S["FA_ERR_SHAPE"]
+    assert bcall(Hq=3) == S["FA_ERR_HEADS"]
+    assert bcall(d=96) == S["FA_ERR_HEADDIM"]
+    assert bcall(dk=0x90000008) == S["FA_ERR_ALIGN"]
+    assert bcall(lse=L + 2) == S["FA_ERR_ALIGN"]
+    assert bcall(scale=float("inf")) == S["FA_ERR_SCALE"]
+    assert bcall(ws=None) == S["FA_ERR_WORKSPACE"]
+    assert bcall(ws_bytes=fa.fa_bwd_workspace_size(2, 4, 16) - 4) == S["FA_ERR_WORKSPACE"]
+    assert bcall(dq=Q) == S["FA_ERR_ALIAS"]
+    assert bcall(dv=0x90000000 + 64) == S["FA_ERR_ALIAS"]       # dv overlaps dk
+    assert bcall(ws=L) == S["FA_ERR_ALIAS"]                      # workspace on lse
+    assert fa.fa_bwd_workspace_size(2, 4, 16) == 2 * 4 * 16 * 4
+    assert fa.fa_bwd_workspace_size(0, 4, 16) == 0
