@@ -18,6 +18,10 @@ kernel sources still hash to the value recorded there (else null).
 cpu_baseline: the fp64 CPU oracle, timed on this host's cores over a bounded
 sample of the same workload's query rows, in the same unit.
 
+--pass bwd times the backward instead (one fa_bwd call per step, the
+forward's o and lse computed once before timing, dO seeded randn), with the
+conventional backward count of 2.5x the forward FLOPs.
+
 --workload picks another named workload.  The split-key ones (unequal query
 and key lengths) run fa_fwd_splitkv, whose step is two launches (the
 split forward and the merge) with the workspace allocated before timing; a
@@ -41,30 +45,56 @@ METRIC = "attn fwd TFLOP/s at N=4096,d=128 causal bf16; % of dense bf16 MFMA pea
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak bandwidth (published)
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILES, "fa_fwd_bf16_causal_B2_H32_N4096_d128_traffic.txt")
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the kernel sources and the public header."""
+def kernel_sources(w, bwd: bool):
+    """The sources a workload's launches depend on: the kernels it runs, the
+    shared internal header, the C-ABI layer and the public header."""
+    if bwd:
+        kern = ["fa_bwd_bf16.hip"]
+    elif w.dtype == "fp32":
+        kern = ["fa_fwd_f32.hip", "fa_combine.hip"]
+    elif w.N * (w.Hq // w.Hkv) <= 64:          # the decoding kernel's shapes
+        kern = ["fa_decode_bf16.hip", "fa_combine.hip"]
+    else:
+        kern = ["fa_fwd_bf16.hip", "fa_combine.hip"]
+    return kern + ["fa_internal.h", "fa_api.cpp"]
+
+
+def kernel_source_hash(names) -> str:
+    """sha256 over the named sources and the public header."""
     from exact_attention_93_amd import _build
     h = hashlib.sha256()
-    for path in _build.sources() + [os.path.join(ROOT, "include", "fa.h")]:
+    for path in [os.path.join(_build.CSRC, n) for n in names] + [os.path.join(ROOT, "include", "fa.h")]:
         with open(path, "rb") as f:
             h.update(os.path.basename(path).encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per launch from the committed counter summary, or None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def traffic_file(w, bwd: bool):
+    """The committed counter summary for this workload, if one is kept."""
+    from exact_attention_93_amd import workloads as W
+    if bwd:
+        return None
+    if w.name == W.HEADLINE:
+        return os.path.join(PROFILES, "fa_fwd_bf16_causal_B2_H32_N4096_d128_traffic.txt")
+    if w.name.startswith("decode_"):
+        return os.path.join(PROFILES, f"fa_decode_bf16_{w.name}_traffic.txt")
+    return None
+
+
+def read_traffic(path, src_hash):
+    """HBM bytes per launch from a committed counter summary taken with the
+    same sources (hash), or None."""
+    if path is None or not os.path.exists(path):
         return None
     kv = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if "=" in line and not line.lstrip().startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_hash") != kernel_source_hash():
+    if kv.get("kernel_source_hash") != src_hash:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -117,12 +147,37 @@ def cpu_baseline(w, seconds: float, hbm: bool):
     }
 
 
+def cpu_baseline_bwd(w, seconds: float, do):
+    """Time the fp64 backward oracle on whole (batch, K/V head) groups."""
+    import oracle
+    from exact_attention_93_amd import workloads as W
+
+    q, k, v = W.gen_inputs(w)
+    threads = oracle.host_threads()
+    groups = [(b, hk) for b in range(w.B) for hk in range(w.Hkv)]
+    t0 = time.perf_counter()
+    oracle.attention_bwd(q, k, v, do, w.scale, w.causal, groups=groups[:1], threads=threads)
+    dt = max(time.perf_counter() - t0, 1e-3)
+    n = int(min(len(groups), max(1, seconds / dt)))
+    pick = groups[:: max(1, len(groups) // n)][:n]
+    t0 = time.perf_counter()
+    oracle.attention_bwd(q, k, v, do, w.scale, w.causal, groups=pick, threads=threads)
+    dt = time.perf_counter() - t0
+    flops = 2.5 * w.flops * len(pick) / len(groups)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(pick)} of the {len(groups)} (batch, K/V head) groups of {w.name} (every gradient "
+                      f"element of those heads); fp64 backward oracle, {dt:.1f} s wall; FLOPs counted as the "
+                      "groups' share of 2.5x the forward count"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline case)")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="time the forward (default) or the backward")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time for cpu_baseline (0: skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain copy of this many MiB (counter calibration runs)")
@@ -165,9 +220,26 @@ def main():
         print(f"# calibration copy: {args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written per neg kernel",
               file=sys.stderr, flush=True)
 
-    def step():
+    bwd = args.which == "bwd"
+    if bwd:
+        if w.dtype != "bf16":
+            raise SystemExit("bench.py: the backward runs on bf16 workloads only")
+        g = torch.Generator(device="cpu").manual_seed(w.seed + 50)
+        do_host = torch.randn(tuple(q.shape), generator=g).to(torch.bfloat16)
+        do = do_host.to(dev)
         fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream,
                num_splits=w.splits, workspace=ws)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.Hq, w.N), dtype=torch.uint8, device=dev)
+        hbm_bound = False
+
+    def step():
+        if bwd:
+            fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=bws,
+                   stream=stream)
+        else:
+            fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream,
+                   num_splits=w.splits, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -187,20 +259,26 @@ def main():
     total_ms = ev[0].elapsed_time(ev[K])
     ms_per_step = total_ms / K
     mean_launch_ms = sum(per) / K
-    if not (torch.isfinite(o.float()).all() and torch.isfinite(lse).all()):
+    outs = (dq, dk, dv) if bwd else (o, lse)
+    if not all(torch.isfinite(t.float()).all() for t in outs):
         print("bench.py: non-finite output", file=sys.stderr)
         sys.exit(1)
 
+    flops = 2.5 * w.flops if bwd else w.flops
     if hbm_bound:
         unit, peak, work = "GB/s", PEAK_HBM_GBS, w.io_bytes / 1e9
     else:
-        unit, peak, work = "TFLOP/s", PEAK_BF16_TFLOPS, w.flops / 1e12
+        unit, peak, work = "TFLOP/s", PEAK_BF16_TFLOPS, flops / 1e12
     value = work / (ms_per_step * 1e-3)
     achieved = work / (mean_launch_ms * 1e-3)
-    headline = w.name == W.HEADLINE
-    traffic = read_traffic() if headline else None
-    metric = METRIC if headline else (
-        f"attn fwd {unit} on {w.name}" + ("; % of HBM peak" if hbm_bound else "; % of dense bf16 MFMA peak"))
+    headline = w.name == W.HEADLINE and not bwd
+    src_hash = kernel_source_hash(kernel_sources(w, bwd))
+    traffic = read_traffic(traffic_file(w, bwd), src_hash)
+    if bwd:
+        metric = f"attn bwd TFLOP/s (2.5x forward FLOPs) on {w.name}; % of dense bf16 MFMA peak"
+    else:
+        metric = METRIC if headline else (
+            f"attn fwd {unit} on {w.name}" + ("; % of HBM peak" if hbm_bound else "; % of dense bf16 MFMA peak"))
     out = {
         "metric": metric,
         "value": round(value, 2),
@@ -216,19 +294,22 @@ def main():
         "data": "synthetic (seeded randn, bf16 round-to-nearest-even)",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                    "causal": w.causal, "io_dtype": w.dtype, "accumulate": "fp32", "layout": "BNHD",
-                   "flops_per_step": w.flops, "pct_of_peak": round(100 * value / peak, 2)},
+                   "flops_per_step": flops, "pct_of_peak": round(100 * value / peak, 2)},
         "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic},
         "timing": {"mean_launch_us": round(mean_launch_ms * 1e3, 2), "min_launch_us": round(min(per) * 1e3, 2),
                    "max_launch_us": round(max(per) * 1e3, 2), "host_wall_s": round(wall, 4),
-                   "kernel_source_hash": kernel_source_hash()},
+                   "kernel_source_hash": src_hash},
     }
     if w.Nkv != w.N or splits > 1:
         out["config"].update({"Nk": w.Nkv, "splits": splits, "algorithmic_bytes_per_step": w.io_bytes})
         out["dtype"] = "bf16" if w.dtype == "bf16" else "f32"
+    if bwd:
+        out["config"]["pass"] = "bwd"
     if args.cpu_seconds > 0:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, hbm_bound)
+        out["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_seconds, do_host) if bwd
+                               else cpu_baseline(w, args.cpu_seconds, hbm_bound))
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
