@@ -44,6 +44,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attn fwd TFLOP/s at N=4096,d=128 causal bf16; % of dense bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak bandwidth (published)
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 matrix-core peak (published)
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -52,6 +53,8 @@ def kernel_sources(w, bwd: bool):
     shared internal header, the C-ABI layer and the public header."""
     if bwd:
         kern = ["fa_bwd_bf16.hip"]
+    elif w.dtype == "fp8":
+        kern = ["fa_fwd_fp8.hip"]
     elif w.dtype == "fp32":
         kern = ["fa_fwd_f32.hip", "fa_combine.hip"]
     elif w.N * (w.Hq // w.Hkv) <= 64:          # the decoding kernel's shapes
@@ -116,7 +119,11 @@ def cpu_baseline(w, seconds: float, hbm: bool):
     import oracle
     from exact_attention_93_amd import workloads as W
 
-    q, k, v = W.gen_inputs(w)
+    if w.dtype == "fp8":
+        q8, k8, v8, qd, kd, vd = W.gen_inputs_fp8(w)
+        q, k, v = W.dequantize_fp8(q8, qd), W.dequantize_fp8(k8, kd), W.dequantize_fp8(v8, vd)
+    else:
+        q, k, v = W.gen_inputs(w)
     bb, hh, ii = np.meshgrid(np.arange(w.B), np.arange(w.Hq), np.arange(w.N), indexing="ij")
     rows = np.stack([bb.ravel(), hh.ravel(), ii.ravel()], axis=1)   # every query row
     threads = oracle.host_threads()
@@ -199,8 +206,13 @@ def main():
 
     w = W.ALL_WORKLOADS[args.workload or W.HEADLINE]
     dev = torch.device("cuda:0")
-    q, k, v = (t.to(dev) for t in W.gen_inputs(w))
-    o = torch.empty_like(q)
+    fp8 = w.dtype == "fp8"
+    if fp8:
+        q, k, v, qd, kd, vd = (t.to(dev) for t in W.gen_inputs_fp8(w))
+        o = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=dev)
+    else:
+        q, k, v = (t.to(dev) for t in W.gen_inputs(w))
+        o = torch.empty_like(q)
     lse = torch.empty((w.B, w.Hq, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     splits = fa.fa_splitkv_num_splits(w.B, w.Hq, w.Hkv, w.N, w.Nkv, w.d, w.splits)
@@ -234,7 +246,9 @@ def main():
         hbm_bound = False
 
     def step():
-        if bwd:
+        if fp8:
+            fa.fwd_fp8(q, k, v, qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        elif bwd:
             fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=bws,
                    stream=stream)
         else:
@@ -268,7 +282,7 @@ def main():
     if hbm_bound:
         unit, peak, work = "GB/s", PEAK_HBM_GBS, w.io_bytes / 1e9
     else:
-        unit, peak, work = "TFLOP/s", PEAK_BF16_TFLOPS, flops / 1e12
+        unit, peak, work = "TFLOP/s", PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS, flops / 1e12
     value = work / (ms_per_step * 1e-3)
     achieved = work / (mean_launch_ms * 1e-3)
     headline = w.name == W.HEADLINE and not bwd
@@ -276,6 +290,8 @@ def main():
     traffic = read_traffic(traffic_file(w, bwd), src_hash)
     if bwd:
         metric = f"attn bwd TFLOP/s (2.5x forward FLOPs) on {w.name}; % of dense bf16 MFMA peak"
+    elif fp8:
+        metric = f"attn fwd TFLOP/s on {w.name} (e4m3 inputs, bf16 output); % of dense fp8 MFMA peak"
     else:
         metric = METRIC if headline else (
             f"attn fwd {unit} on {w.name}" + ("; % of HBM peak" if hbm_bound else "; % of dense bf16 MFMA peak"))
@@ -307,6 +323,10 @@ def main():
         out["dtype"] = "bf16" if w.dtype == "bf16" else "f32"
     if bwd:
         out["config"]["pass"] = "bwd"
+    if fp8:
+        out["dtype"] = "fp8-e4m3"
+        out["data"] = "synthetic (seeded randn, e4m3 round-to-nearest-even with one scale per (batch, head))"
+        out["config"].update({"io_dtype": "e4m3 in, bf16 out", "descale": "per (batch, head)"})
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_seconds, do_host) if bwd
                                else cpu_baseline(w, args.cpu_seconds, hbm_bound))

@@ -29,7 +29,7 @@ import os
 
 from ._build import LIB_PATH
 
-__all__ = ["fwd", "bwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_splitkv_num_splits",
+__all__ = ["fwd", "fwd_fp8", "fa_fwd_fp8", "bwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_splitkv_num_splits",
            "fa_splitkv_workspace_size", "fa_strerror", "fa_version", "load_library", "FAError",
            "STATUS", "EXPORTS"]
 
@@ -39,7 +39,8 @@ STATUS = {
     "FA_ERR_SPLITS": 9, "FA_ERR_WORKSPACE": 10,
 }
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_splitkv_num_splits",
-           "fa_splitkv_workspace_size", "fa_bwd", "fa_bwd_workspace_size", "fa_strerror", "fa_version")
+           "fa_splitkv_workspace_size", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_size", "fa_strerror",
+           "fa_version")
 
 _lib = None
 
@@ -75,6 +76,9 @@ def load_library(path: str = LIB_PATH):
     lib.fa_splitkv_num_splits.argtypes = [ctypes.c_int] * 7
     lib.fa_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.fa_splitkv_workspace_size.argtypes = [ctypes.c_int] * 7
+    lib.fa_fwd_fp8.restype = ctypes.c_int
+    lib.fa_fwd_fp8.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
+                               ctypes.c_void_p])
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 9 + [ctypes.c_int] * 6 + [ctypes.c_float, ctypes.c_int,
                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
@@ -217,3 +221,47 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
     if st != 0:
         raise FAError(st, fa_strerror(st))
     return dq, dk, dv
+
+
+def fa_fwd_fp8(q, k, v, qd, kd, vd, o, lse, B, Hq, Hkv, N, d, scale, causal, stream) -> int:
+    return load_library().fa_fwd_fp8(q, k, v, qd, kd, vd, o, lse, B, Hq, Hkv, N, d, float(scale), int(causal),
+                                     stream)
+
+
+def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal: bool = False, scale: float | None = None,
+            out=None, lse=None, stream=None):
+    """fp8 (e4m3) attention forward through libfa.so.  Returns (o bf16, lse).
+
+    q: [B, N, Hq, d], k, v: [B, N, Hkv, d] as torch.float8_e4m3fn (or uint8
+    codes); q_descale [B, Hq], k_descale and v_descale [B, Hkv] float32: the
+    real inputs are code * descale."""
+    import torch
+
+    ts = (q, k, v, q_descale, k_descale, v_descale)
+    if not all(t.is_cuda for t in ts):
+        raise ValueError("fwd_fp8: every tensor must be on the GPU (there is no CPU path)")
+    if any(t.element_size() != 1 for t in (q, k, v)):
+        raise ValueError("fwd_fp8: q, k, v must hold one-byte e4m3 codes")
+    if any(t.dtype != torch.float32 for t in ts[3:]):
+        raise ValueError("fwd_fp8: descale factors must be float32")
+    if not all(t.is_contiguous() for t in ts):
+        raise ValueError("fwd_fp8: tensors must be contiguous")
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    if (tuple(k.shape) != (B, N, Hkv, d) or v.shape != k.shape or tuple(q_descale.shape) != (B, Hq)
+            or tuple(k_descale.shape) != (B, Hkv) or tuple(v_descale.shape) != (B, Hkv)):
+        raise ValueError("fwd_fp8: shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, N, Hq, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(),
+                    v_descale.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d, scale, causal,
+                    stream.cuda_stream)
+    if st != 0:
+        raise FAError(st, fa_strerror(st))
+    return out, lse

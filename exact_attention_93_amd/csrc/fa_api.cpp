@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 102;  // 0.1.2
+constexpr int kVersion = 103;  // 0.1.3
 constexpr int kMaxSplits = 256;
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb)
@@ -71,7 +71,8 @@ size_t workspace_bytes_for(int B, int Hq, int Nq, int d, int nsplit)
 
 int validate_and_fill(const void *q, const void *k, const void *v, void *o, float *lse,
                       int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
-                      int num_splits, void *ws, size_t ws_bytes, size_t elem, fa::FwdParams &p)
+                      int num_splits, void *ws, size_t ws_bytes, size_t elem, fa::FwdParams &p,
+                      size_t out_elem = 0)
 {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
@@ -93,20 +94,23 @@ int validate_and_fill(const void *q, const void *k, const void *v, void *o, floa
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_ALIGN;
     if ((uintptr_t)lse & 3) return FA_ERR_ALIGN;
     if (!isfinite(scale)) return FA_ERR_SCALE;
+    if (out_elem == 0) out_elem = elem;
     const size_t nq = (size_t)B * Nq * Hq * d * elem;
+    const size_t no = (size_t)B * Nq * Hq * d * out_elem;
     const size_t nk = (size_t)B * Nk * Hkv * d * elem;
     const size_t nl = (size_t)B * Hq * Nq * sizeof(float);
-    if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nk) || overlaps(o, nq, v, nk) ||
+    if (overlaps(o, no, q, nq) || overlaps(o, no, k, nk) || overlaps(o, no, v, nk) ||
         overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nk) || overlaps(lse, nl, v, nk) ||
-        overlaps(o, nq, lse, nl))
+        overlaps(o, no, lse, nl))
         return FA_ERR_ALIAS;
     p.o_part = nullptr;
     p.lse_part = nullptr;
+    p.q_descale = p.k_descale = p.v_descale = nullptr;
     if (nsplit > 1) {
         const size_t need = workspace_bytes_for(B, Hq, Nq, d, nsplit);
         if (!ws || ws_bytes < need || ((uintptr_t)ws & 15)) return FA_ERR_WORKSPACE;
         if (overlaps(ws, need, q, nq) || overlaps(ws, need, k, nk) || overlaps(ws, need, v, nk) ||
-            overlaps(ws, need, o, nq) || overlaps(ws, need, lse, nl))
+            overlaps(ws, need, o, no) || overlaps(ws, need, lse, nl))
             return FA_ERR_ALIAS;
         p.o_part = (float *)ws;
         p.lse_part = (float *)ws + (size_t)nsplit * B * Hq * Nq * d;
@@ -207,6 +211,23 @@ size_t fa_splitkv_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, 
     const int nsplit = fa_splitkv_num_splits(B, Hq, Hkv, Nq, Nk, d, num_splits);
     if (nsplit <= 1) return 0;
     return workspace_bytes_for(B, Hq, Nq, d, nsplit);
+}
+
+int fa_fwd_fp8(const void *q, const void *k, const void *v, const float *q_descale,
+               const float *k_descale, const float *v_descale, void *o, float *lse, int B, int Hq,
+               int Hkv, int N, int d, float scale, int causal, void *stream)
+{
+    if (!q_descale || !k_descale || !v_descale) return FA_ERR_NULL;
+    if (d != 128) return (!q || !k || !v || !o || !lse) ? FA_ERR_NULL : FA_ERR_HEADDIM;
+    if (((uintptr_t)q_descale | (uintptr_t)k_descale | (uintptr_t)v_descale) & 3) return FA_ERR_ALIGN;
+    fa::FwdParams p;
+    const int st = validate_and_fill(q, k, v, o, lse, B, Hq, Hkv, N, N, d, scale, causal, 1,
+                                     nullptr, 0, 1, p, 2);
+    if (st != FA_OK) return st;
+    p.q_descale = q_descale;
+    p.k_descale = k_descale;
+    p.v_descale = v_descale;
+    return fa::launch_fwd_fp8(p, d, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 size_t fa_bwd_workspace_size(int B, int Hq, int Nq)

@@ -28,9 +28,14 @@ struct FwdParams {
     int xcd_groups;   // 1 when B*Hkv is a multiple of 8 (one XCD per head group)
     int qmode;        // 0: q as given; 1: q negated (scale < 0); 2: q zeroed (scale == 0)
     float c;          // |scale| * log2(e) (positive), or 1 when scale == 0
+    // fp8 forward: dequantisation factors per (batch, head), real value = code * factor
+    const float *q_descale;   // [B][Hq]
+    const float *k_descale;   // [B][Hkv]
+    const float *v_descale;   // [B][Hkv]
 };
 
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, hipStream_t stream);
+hipError_t launch_fwd_fp8(const FwdParams &p, int d, hipStream_t stream);
 // Few query rows per K/V head (decoding): rows of one head group packed into
 // 32-row blocks, K/V read once per group.
 hipError_t launch_decode_bf16(const FwdParams &p, int d, hipStream_t stream);

@@ -28,7 +28,7 @@ class Workload:
     Hkv: int
     N: int
     d: int
-    dtype: str          # "fp32" or "bf16"
+    dtype: str          # "fp32", "bf16" or "fp8"
     causal: bool
     q_std: float
     seed: int
@@ -68,9 +68,11 @@ class Workload:
 
     @property
     def io_bytes(self) -> int:
-        """Bytes the forward must move at least once: q, k, v read, o and lse written."""
-        s = 4 if self.dtype == "fp32" else 2
-        return ((2 * self.Hq * self.N + 2 * self.Hkv * self.Nkv) * self.B * self.d * s
+        """Bytes the forward must move at least once: q, k, v read, o and lse written
+        (fp8: one-byte inputs, bf16 output)."""
+        s_in = {"fp32": 4, "fp8": 1}.get(self.dtype, 2)
+        s_out = 4 if self.dtype == "fp32" else 2
+        return ((self.Hq * self.N * (s_in + s_out) + 2 * self.Hkv * self.Nkv * s_in) * self.B * self.d
                 + 4 * self.B * self.Hq * self.N)
 
 
@@ -97,7 +99,13 @@ SPLIT_WORKLOADS = {
         "chunk_causal_bf16_B1_H32_Nq1024_Nk16384_d128", 1, 32, 32, 1024, 128, "bf16", True, 1.0, 1007,
         Nk=16384, splits=0),
 }
-ALL_WORKLOADS = {**WORKLOADS, **SPLIT_WORKLOADS}
+# fp8 (e4m3) inputs with one dequantisation factor per (batch, head), on the
+# headline shape.
+FP8_WORKLOADS = {
+    "causal_fp8_B2_H32_N4096_d128": Workload(
+        "causal_fp8_B2_H32_N4096_d128", 2, 32, 32, 4096, 128, "fp8", True, 1.0, 1008),
+}
+ALL_WORKLOADS = {**WORKLOADS, **SPLIT_WORKLOADS, **FP8_WORKLOADS}
 
 
 def make(B, Hq, Hkv, N, d, dtype="bf16", causal=False, q_std=1.0, seed=0, name="custom", Nk=0,
@@ -118,6 +126,36 @@ def gen_inputs(w: Workload):
     elif w.dtype != "fp32":
         raise ValueError(w.dtype)
     return q.contiguous(), k.contiguous(), v.contiguous()
+
+
+def quantize_fp8(x: torch.Tensor):
+    """Per-(batch, head) e4m3 quantisation of a float [B, N, H, d] tensor.
+
+    descale = amax / 440 over each (b, h) slice (a little headroom below the
+    format's 448), codes = round-to-nearest-even e4m3 of x / descale.  Returns
+    (codes as torch.float8_e4m3fn [B, N, H, d], descale float32 [B, H])."""
+    amax = x.abs().amax(dim=(1, 3)).clamp(min=1e-12)          # [B, H]
+    descale = (amax / 440.0).to(torch.float32)
+    codes = (x / descale[:, None, :, None]).to(torch.float8_e4m3fn)
+    return codes.contiguous(), descale.contiguous()
+
+
+def gen_inputs_fp8(w: Workload):
+    """fp8 workload inputs: the same seeded randn draws as gen_inputs, then
+    quantize_fp8 on each of q, k, v.  Returns (q8, k8, v8, q_descale,
+    k_descale, v_descale)."""
+    g = torch.Generator(device="cpu").manual_seed(w.seed)
+    q = torch.randn((w.B, w.N, w.Hq, w.d), generator=g, dtype=torch.float32) * w.q_std
+    k = torch.randn((w.B, w.Nkv, w.Hkv, w.d), generator=g, dtype=torch.float32)
+    v = torch.randn((w.B, w.Nkv, w.Hkv, w.d), generator=g, dtype=torch.float32)
+    (q8, qd), (k8, kd), (v8, vd) = quantize_fp8(q), quantize_fp8(k), quantize_fp8(v)
+    return q8, k8, v8, qd, kd, vd
+
+
+def dequantize_fp8(codes: torch.Tensor, descale: torch.Tensor) -> torch.Tensor:
+    """The real values code * descale as float32 [B, N, H, d] (the e4m3 code
+    widens exactly; the product is rounded once to float32)."""
+    return (codes.to(torch.float32) * descale[:, None, :, None]).contiguous()
 
 
 def sample_rows(w: Workload, per_head: int = 512, seed: int | None = None):

@@ -145,6 +145,27 @@ int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num
 size_t fa_splitkv_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
 
 /*
+ * fa_fwd_fp8 -- the forward with fp8 inputs: the low-precision path of the
+ * second page's section 10 (FlashAttention-3 FP8) with per-block scales
+ * (section 12.2), one block per (batch, head).
+ *   q, k, v   : OCP e4m3 (E4M3FN) codes, one byte per element, laid out as
+ *               fa_fwd's q, k, v.  The real inputs are code * descale:
+ *   q_descale : fp32 [B][Hq], k_descale and v_descale : fp32 [B][Hkv] (device).
+ *   o         : bf16 [B][N][Hq][d], round to nearest even.
+ *   lse       : fp32 [B][Hq][N], of the real scaled scores.
+ * The scores come from the fp8 matrix cores (exact products, fp32 sums).  The
+ * probabilities are quantised to e4m3 for the P V product (relative error at
+ * most 2^-4 each, against a running maximum so that none saturates), and O
+ * is normalised by the sum of the quantised values, so every output row is a
+ * convex combination of V rows with weights within 2^-4 of the exact ones.
+ * d must be 128.  Other arguments, errors and limits as for fa_fwd; the
+ * descale pointers must be non-NULL and 4-byte aligned.
+ */
+int fa_fwd_fp8(const void *q, const void *k, const void *v, const float *q_descale,
+               const float *k_descale, const float *v_descale, void *o, float *lse,
+               int B, int Hq, int Hkv, int N, int d, float scale, int causal, void *stream);
+
+/*
  * fa_bwd -- gradients of the bf16 forward (fa_fwd / fa_fwd_splitkv) for an
  * upstream gradient dout = dL/do.
  *

@@ -46,7 +46,7 @@ def test_status_codes_match_header():
 
 
 def test_version_and_strerror(lib):
-    assert fa.fa_version() == 102
+    assert fa.fa_version() == 103
     for st in range(11):
         assert fa.fa_strerror(st)
     assert "unknown" in fa.fa_strerror(99)
@@ -180,3 +180,23 @@ def test_invalid_arguments_bwd(lib):
     assert bcall(ws=L) == S["FA_ERR_ALIAS"]                      # workspace on lse
     assert fa.fa_bwd_workspace_size(2, 4, 16) == 2 * 4 * 16 * 4
     assert fa.fa_bwd_workspace_size(0, 4, 16) == 0
+
+
+def test_invalid_arguments_fp8(lib):
+    S = fa.STATUS
+    QD, KD, VD = 0xB0000000, 0xB0001000, 0xB0002000
+
+    def fcall(q=Q, k=K, v=V, qd=QD, kd=KD, vd=VD, o=O, lse=L, **kw):
+        a = dict(B=1, Hq=4, Hkv=2, N=16, d=128, scale=0.1, causal=1)
+        a.update(kw)
+        return fa.fa_fwd_fp8(q, k, v, qd, kd, vd, o, lse, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["scale"],
+                             a["causal"], None)
+    assert fcall(qd=None) == S["FA_ERR_NULL"]
+    assert fcall(v=None) == S["FA_ERR_NULL"]
+    assert fcall(d=64) == S["FA_ERR_HEADDIM"]
+    assert fcall(kd=KD + 2) == S["FA_ERR_ALIGN"]
+    assert fcall(q=Q + 4) == S["FA_ERR_ALIGN"]
+    assert fcall(N=0) == S["FA_ERR_SHAPE"]
+    assert fcall(Hq=3) == S["FA_ERR_HEADS"]
+    assert fcall(scale=float("nan")) == S["FA_ERR_SCALE"]
+    assert fcall(o=Q + 1024) == S["FA_ERR_ALIAS"]      # bf16 output running over the fp8 q
