@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 103;  // 0.1.3
+constexpr int kVersion = 104;  // 0.1.4
 constexpr int kMaxSplits = 256;
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb)
@@ -72,12 +72,12 @@ size_t workspace_bytes_for(int B, int Hq, int Nq, int d, int nsplit)
 int validate_and_fill(const void *q, const void *k, const void *v, void *o, float *lse,
                       int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                       int num_splits, void *ws, size_t ws_bytes, size_t elem, fa::FwdParams &p,
-                      size_t out_elem = 0)
+                      size_t out_elem = 0, bool allow_d256 = false)
 {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
     if (Hq % Hkv != 0) return FA_ERR_HEADS;
-    if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+    if (d != 64 && d != 128 && !(allow_d256 && d == 256)) return FA_ERR_HEADDIM;
     if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_SPLITS;
     if (num_splits == 0) num_splits = heuristic_splits(B, Hq, Hkv, Nq, Nk);
     int split_keys, nsplit;
@@ -146,7 +146,7 @@ int run(const fa::FwdParams &p, int d, bool bf16, hipStream_t stream)
 {
     hipError_t e;
     if (!bf16) e = fa::launch_fwd_f32(p, d, stream);
-    else if (fa::use_decode(p.Nq, p.group)) e = fa::launch_decode_bf16(p, d, stream);
+    else if (d <= 128 && fa::use_decode(p.Nq, p.group)) e = fa::launch_decode_bf16(p, d, stream);
     else e = fa::launch_fwd_bf16(p, d, stream);
     if (e != hipSuccess) return FA_ERR_LAUNCH;
     if (p.nsplit > 1 && fa::launch_combine(p, d, bf16 ? 1 : 0, stream) != hipSuccess) return FA_ERR_LAUNCH;
@@ -162,7 +162,7 @@ int fa_fwd(const void *q, const void *k, const void *v, void *o, float *lse,
 {
     fa::FwdParams p;
     const int st = validate_and_fill(q, k, v, o, lse, B, Hq, Hkv, N, N, d, scale, causal, 1,
-                                     nullptr, 0, 2, p);
+                                     nullptr, 0, 2, p, 0, true);
     return st != FA_OK ? st : run(p, d, true, (hipStream_t)stream);
 }
 
@@ -181,7 +181,7 @@ int fa_fwd_splitkv(const void *q, const void *k, const void *v, void *o, float *
 {
     fa::FwdParams p;
     const int st = validate_and_fill(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal,
-                                     num_splits, workspace, workspace_bytes, 2, p);
+                                     num_splits, workspace, workspace_bytes, 2, p, 0, true);
     return st != FA_OK ? st : run(p, d, true, (hipStream_t)stream);
 }
 
@@ -198,7 +198,7 @@ int fa_fwd_splitkv_f32(const float *q, const float *k, const float *v, float *o,
 int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits)
 {
     if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || Hq % Hkv != 0) return -FA_ERR_SHAPE;
-    if (d != 64 && d != 128) return -FA_ERR_HEADDIM;
+    if (d != 64 && d != 128 && d != 256) return -FA_ERR_HEADDIM;
     if (num_splits < 0 || num_splits > kMaxSplits) return -FA_ERR_SPLITS;
     if (num_splits == 0) num_splits = heuristic_splits(B, Hq, Hkv, Nq, Nk);
     int split_keys, nsplit;
@@ -299,7 +299,7 @@ const char *fa_strerror(int status)
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "B, Hq, Hkv and the sequence lengths must be >= 1 and within the size limits";
     case FA_ERR_HEADS: return "Hq must be a multiple of Hkv";
-    case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
+    case FA_ERR_HEADDIM: return "unsupported head dimension (bf16 forward: 64, 128, 256; fp32 forward and backward: 64, 128; fp8: 128)";
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_SCALE: return "scale must be finite (and |scale|*log2(e) representable)";
     case FA_ERR_ALIAS: return "an output or the workspace overlaps an input or another output";

@@ -131,6 +131,7 @@ hipError_t launch_one(const FwdParams &p, hipStream_t stream)
 
 hipError_t launch_combine(const FwdParams &p, int d, int out_bf16, hipStream_t stream)
 {
+    if (d == 256) return out_bf16 ? launch_one<256, true>(p, stream) : launch_one<256, false>(p, stream);
     if (d == 128) return out_bf16 ? launch_one<128, true>(p, stream) : launch_one<128, false>(p, stream);
     return out_bf16 ? launch_one<64, true>(p, stream) : launch_one<64, false>(p, stream);
 }

@@ -76,9 +76,14 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr int kBM = 256;       // query rows per workgroup: 8 wavefronts x 32
 constexpr int kBN = 64;        // keys per K/V tile
-constexpr int kThreads = 512;  // 8 wavefronts of 64
+// Wavefronts per workgroup: 8 (two per SIMD, the two groups of the
+// ping-pong), or 4 at d = 256, where one wavefront's Q and O^T alone take
+// 192 registers and a single wavefront per SIMD gets the whole register
+// file (the two groups then coincide and the phases run back to back).
+template <int D> constexpr int wg_waves() { return D == 256 ? 4 : 8; }
+template <int D> constexpr int wg_threads() { return 64 * wg_waves<D>(); }
+template <int D> constexpr int wg_rows() { return 32 * wg_waves<D>(); }   // query rows per workgroup
 constexpr float kLazyLog2 = 8.0f;
 constexpr float kFarSum = 0x1p64f;   // tile row sum that signals a stale reference maximum
 constexpr int PF_PV = 4;       // products whose V^T operands are read ahead of the matrix cores
@@ -124,13 +129,15 @@ __device__ __forceinline__ float sum_halves(float x)
 // K: the 16 rows one phase of a 16-byte operand read touches land in 16
 // distinct bank groups.  V: the 4 rows x 4 chunks one phase of the transpose
 // read touches land in 16 distinct bank groups.
+// (d = 256 rows span two 256-byte bank windows; only the chunk index mod 16
+// decides the bank group, so the d = 128 permutations serve.)
 template <int D> __device__ __forceinline__ int k_swz(int row)
 {
-    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+    return D != 64 ? (row & 15) : ((row >> 1) & 7);
 }
 template <int D> __device__ __forceinline__ int v_swz(int row)
 {
-    return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+    return D != 64 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
 // 16 bytes per lane from base + off (bytes) straight into LDS at dst + 16*lane,
@@ -148,8 +155,10 @@ __device__ __forceinline__ void lds_wait_vm()
 }
 
 template <int D, bool CAUSAL, bool SPLIT>
-__global__ void __launch_bounds__(kThreads, 1) fwd_bf16_kernel(FwdParams p)
+__global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams p)
 {
+    constexpr int kThreads = wg_threads<D>();
+    constexpr int kBM = wg_rows<D>();
     constexpr int KSTEPS = D / 16;                 // K-steps of S^T = K Q^T
     constexpr int XB = D / 32;                     // 32-row blocks of O^T
     constexpr int NKB = kBN / 32;                  // 32-key blocks per tile
@@ -177,7 +186,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_bf16_kernel(FwdParams p)
     const int hk = h / p.group;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int grp = wave >> 2;                    // 0: leading group, 1: trailing group
+    const int grp = wave >> 2;                    // 0: leading group, 1: trailing group (8 wavefronts)
     const int lq = lane & 31, hf = lane >> 5;
     const int Nq = p.Nq, Nk = p.Nk, off = p.off;
     const int q_first = tile * kBM;
@@ -499,10 +508,12 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_bf16_kernel(FwdParams p)
 }
 
 template <int D, bool CAUSAL, bool SPLIT>
-hipError_t launch_one(const FwdParams &p, hipStream_t stream)
+hipError_t launch_one(const FwdParams &p_in, hipStream_t stream)
 {
+    FwdParams p = p_in;
+    p.ntiles = (p.Nq + wg_rows<D>() - 1) / wg_rows<D>();
     const unsigned grid = (unsigned)p.B * (unsigned)p.Hq * (unsigned)p.ntiles * (unsigned)p.nsplit;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPLIT>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPLIT>), dim3(grid), dim3(wg_threads<D>()), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -516,10 +527,9 @@ hipError_t launch_d(const FwdParams &p, hipStream_t stream)
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdParams &p_in, int d, hipStream_t stream)
+hipError_t launch_fwd_bf16(const FwdParams &p, int d, hipStream_t stream)
 {
-    FwdParams p = p_in;
-    p.ntiles = (p.Nq + kBM - 1) / kBM;
+    if (d == 256) return launch_d<256>(p, stream);
     return d == 128 ? launch_d<128>(p, stream) : launch_d<64>(p, stream);
 }
 

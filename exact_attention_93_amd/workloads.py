@@ -105,7 +105,12 @@ FP8_WORKLOADS = {
     "causal_fp8_B2_H32_N4096_d128": Workload(
         "causal_fp8_B2_H32_N4096_d128", 2, 32, 32, 4096, 128, "fp8", True, 1.0, 1008),
 }
-ALL_WORKLOADS = {**WORKLOADS, **SPLIT_WORKLOADS, **FP8_WORKLOADS}
+# Head dimension 256 (the FLOP count of the headline case, half the heads).
+D256_WORKLOADS = {
+    "causal_bf16_B2_H16_N4096_d256": Workload(
+        "causal_bf16_B2_H16_N4096_d256", 2, 16, 16, 4096, 256, "bf16", True, 1.0, 1009),
+}
+ALL_WORKLOADS = {**WORKLOADS, **SPLIT_WORKLOADS, **FP8_WORKLOADS, **D256_WORKLOADS}
 
 
 def make(B, Hq, Hkv, N, d, dtype="bf16", causal=False, q_std=1.0, seed=0, name="custom", Nk=0,

@@ -44,7 +44,9 @@
  * propagate into the results (no check is made).  No C++ exception crosses
  * this interface.
  *
- * Limits.  d in {64, 128}; B, Hq, Hkv, Nq, Nk >= 1; Hq % Hkv == 0;
+ * Limits.  d in {64, 128, 256} for the bf16 forward (fa_fwd, fa_fwd_splitkv),
+ * {64, 128} for the fp32 forward and the backward, 128 for fa_fwd_fp8;
+ * B, Hq, Hkv, Nq, Nk >= 1; Hq % Hkv == 0;
  * (Nq + 256) * Hq * d < 2^29 and (Nk + 256) * Hkv * d < 2^29 (elements per
  * batch entry of one tensor); B * Hq * ceil(Nq / 128) * splits < 2^31.
  */
@@ -62,7 +64,7 @@ typedef enum {
     FA_ERR_NULL = 1,     /* a required pointer is NULL                          */
     FA_ERR_SHAPE = 2,    /* B, Hq, Hkv or N < 1, or a size limit exceeded        */
     FA_ERR_HEADS = 3,    /* Hq is not a multiple of Hkv                          */
-    FA_ERR_HEADDIM = 4,  /* d is not 64 or 128                                   */
+    FA_ERR_HEADDIM = 4,  /* d not supported by this entry point (see Limits)      */
     FA_ERR_ALIGN = 5,    /* q, k, v or o not 16-byte aligned; lse not 4-byte     */
     FA_ERR_SCALE = 6,    /* scale not finite, or |scale|*log2(e) not a normal float (scale 0 is allowed) */
     FA_ERR_ALIAS = 7,    /* o or lse overlaps q, k, v or each other              */

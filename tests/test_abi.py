@@ -46,7 +46,7 @@ def test_status_codes_match_header():
 
 
 def test_version_and_strerror(lib):
-    assert fa.fa_version() == 103
+    assert fa.fa_version() == 104
     for st in range(11):
         assert fa.fa_strerror(st)
     assert "unknown" in fa.fa_strerror(99)
@@ -74,7 +74,8 @@ def test_invalid_arguments(lib, entry):
         assert call(entry, **bad) == S["FA_ERR_SHAPE"], bad
     assert call(entry, N=1 << 20, Hq=32, Hkv=32, d=128) == S["FA_ERR_SHAPE"]
     assert call(entry, Hq=6, Hkv=4) == S["FA_ERR_HEADS"]
-    for d in (0, 32, 96, 256):
+    bad_d = (0, 32, 96, 512) if entry is fa.fa_fwd else (0, 32, 96, 256, 512)   # bf16 takes d = 256
+    for d in bad_d:
         assert call(entry, d=d) == S["FA_ERR_HEADDIM"], d
     assert call(entry, q=Q + 8) == S["FA_ERR_ALIGN"]
     assert call(entry, o=O + 2) == S["FA_ERR_ALIGN"]
@@ -113,7 +114,11 @@ def test_invalid_arguments_split(lib, entry):
     assert scall(entry, Nk=1 << 20, Hkv=32, Hq=32, d=128) == S["FA_ERR_SHAPE"]
     assert scall(entry, Nq=1 << 20, Hkv=1, Hq=32, d=128) == S["FA_ERR_SHAPE"]
     assert scall(entry, Hq=3) == S["FA_ERR_HEADS"]
-    assert scall(entry, d=256) == S["FA_ERR_HEADDIM"]
+    assert scall(entry, d=512) == S["FA_ERR_HEADDIM"]
+    if entry is fa.fa_fwd_splitkv_f32:
+        assert scall(entry, d=256) == S["FA_ERR_HEADDIM"]
+    else:   # d = 256 passes the head-dim check; keep another argument invalid so nothing launches
+        assert scall(entry, d=256, q=Q + 8) == S["FA_ERR_ALIGN"]
     for ns in (-1, 257, 1 << 30):
         assert scall(entry, ns=ns) == S["FA_ERR_SPLITS"], ns
     need = fa.fa_splitkv_workspace_size(2, 4, 2, 16, 300, 64, 3)
@@ -170,6 +175,7 @@ def test_invalid_arguments_bwd(lib):
     assert bcall(Nk=1 << 20, Hkv=32, Hq=32, d=128) == S["FA_ERR_SHAPE"]
     assert bcall(Hq=3) == S["FA_ERR_HEADS"]
     assert bcall(d=96) == S["FA_ERR_HEADDIM"]
+    assert bcall(d=256) == S["FA_ERR_HEADDIM"]
     assert bcall(dk=0x90000008) == S["FA_ERR_ALIGN"]
     assert bcall(lse=L + 2) == S["FA_ERR_ALIGN"]
     assert bcall(scale=float("inf")) == S["FA_ERR_SCALE"]
