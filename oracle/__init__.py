@@ -50,6 +50,11 @@ def _open(path):
     f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 6 + [
         ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    f = lib.oracle_attention_masked
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 6 + [
+        ctypes.c_double, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+        ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     f = lib.oracle_attention_bwd
     f.restype = ctypes.c_int
     f.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] * 6 + [
@@ -88,7 +93,8 @@ def _as_f32(x) -> np.ndarray:
     return x
 
 
-def attention(q, k, v, scale, causal=False, rows=None, threads=None, _lib_override=None):
+def attention(q, k, v, scale, causal=False, rows=None, threads=None, _lib_override=None,
+              block_mask=None, block=(128, 64)):
     """Exact attention forward, fp64, for selected query rows.
 
     q: [B, Nq, Hq, d]; k, v: [B, Nk, Hkv, d] (float32 arrays or bf16/fp32
@@ -96,7 +102,10 @@ def attention(q, k, v, scale, causal=False, rows=None, threads=None, _lib_overri
     it).  causal: key j visible to query i iff j <= i + Nk - Nq (bottom-right
     alignment); a row that sees no key gives O = 0, lse = -inf.
     rows: int array [R, 3] of (b, h, i); None means every row, in (b, h, i)
-    order.  Returns (o [R, d] float64, lse [R] float64).
+    order.  block_mask: None, or a uint8 array [Hq, ceil(Nq/bq), ceil(Nk/bk)]
+    with block = (bq, bk): key j is kept for query i of head h only where the
+    mask entry of their blocks is nonzero.  Returns (o [R, d] float64,
+    lse [R] float64).
     ``_lib_override`` lets the mutation tests run a deliberately broken copy.
     """
     lib = _lib_override if _lib_override is not None else _load()
@@ -114,9 +123,19 @@ def attention(q, k, v, scale, causal=False, rows=None, threads=None, _lib_overri
     lse = np.empty(R, dtype=np.float64)
     sc = float(np.float32(scale))
     nt = threads or host_threads()
-    rc = lib.oracle_attention(q.ctypes.data, k.ctypes.data, v.ctypes.data,
-                              B, Hq, Hkv, Nq, Nk, d, sc, int(bool(causal)),
-                              rows.ctypes.data, R, o.ctypes.data, lse.ctypes.data, nt)
+    if block_mask is None:
+        rc = lib.oracle_attention(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                  B, Hq, Hkv, Nq, Nk, d, sc, int(bool(causal)),
+                                  rows.ctypes.data, R, o.ctypes.data, lse.ctypes.data, nt)
+    else:
+        bq, bk = int(block[0]), int(block[1])
+        m = block_mask.detach().cpu().numpy() if hasattr(block_mask, "detach") else block_mask
+        m = np.ascontiguousarray(np.asarray(m, dtype=np.uint8))
+        if m.shape != (Hq, -(-Nq // bq), -(-Nk // bk)):
+            raise ValueError(f"block mask shape {m.shape} does not match the blocks")
+        rc = lib.oracle_attention_masked(q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                         B, Hq, Hkv, Nq, Nk, d, sc, int(bool(causal)), m.ctypes.data, bq, bk,
+                                         rows.ctypes.data, R, o.ctypes.data, lse.ctypes.data, nt)
     if rc != 0:
         raise RuntimeError(f"oracle_attention failed with code {rc}")
     return o, lse

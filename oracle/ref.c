@@ -29,6 +29,11 @@
  * With Nq == Nk this is j <= i.  A query that sees no key (possible when
  * Nq > Nk) gets an all-zero output row, as that section states, and
  * lse = -inf (the log of an empty sum).
+ *
+ * Block-sparse attention (first page, section 0x04: blocks that a sparsity
+ * pattern marks are skipped entirely): with a block mask, key j is kept for
+ * query i of head h only if mask[h][i / bq][j / bk] is nonzero, in addition
+ * to the causal rule; the softmax runs over the kept keys alone.
  */
 #include <math.h>
 #include <pthread.h>
@@ -41,6 +46,8 @@ typedef struct {
     int B, Hq, Hkv, Nq, Nk, d;
     double scale;
     int causal;
+    const uint8_t *mask; /* optional block mask [Hq][ceil(Nq/bq)][ceil(Nk/bk)] */
+    int bq, bk;
     const int32_t *rows; /* triples (b, h, i) */
     int64_t nrows;
     double *o;   /* [nrows][d] */
@@ -48,6 +55,14 @@ typedef struct {
     int64_t next;
     pthread_mutex_t lock;
 } job_t;
+
+/* Whether the block mask (if any) keeps key j for query i of head h. */
+static int kept(const job_t *J, int h, int i, int j)
+{
+    if (!J->mask) return 1;
+    const int64_t nqb = (J->Nq + J->bq - 1) / J->bq, nkb = (J->Nk + J->bk - 1) / J->bk;
+    return J->mask[((int64_t)h * nqb + i / J->bq) * nkb + j / J->bk] != 0;
+}
 
 /* One query row, the three passes of the safe softmax, then P V. */
 static void one_row(const job_t *J, int b, int h, int i, double *s,
@@ -62,7 +77,9 @@ static void one_row(const job_t *J, int b, int h, int i, double *s,
         const int64_t last = (int64_t)i + (J->Nk - J->Nq);
         nvis = last < 0 ? 0 : (last + 1 < J->Nk ? (int)(last + 1) : J->Nk);
     }
-    if (nvis == 0) {                        /* empty row: zero output */
+    int nkept = 0;
+    for (int j = 0; j < nvis; ++j) nkept += kept(J, h, i, j);
+    if (nkept == 0) {                       /* empty row: zero output */
         for (int x = 0; x < d; ++x) o_out[x] = 0.0;
         *lse_out = -INFINITY;
         return;
@@ -70,6 +87,7 @@ static void one_row(const job_t *J, int b, int h, int i, double *s,
 
     /* scores s_j = scale * <q_i, k_j> for the visible keys */
     for (int j = 0; j < nvis; ++j) {
+        if (!kept(J, h, i, j)) continue;
         const float *kj = J->k + (((int64_t)b * J->Nk + j) * J->Hkv + hk) * d;
         double acc = 0.0;
         for (int x = 0; x < d; ++x)
@@ -79,14 +97,15 @@ static void one_row(const job_t *J, int b, int h, int i, double *s,
     /* pass 1: row maximum */
     double m = -INFINITY;
     for (int j = 0; j < nvis; ++j)
-        if (s[j] > m) m = s[j];
+        if (kept(J, h, i, j) && s[j] > m) m = s[j];
     /* pass 2: normaliser */
     double l = 0.0;
     for (int j = 0; j < nvis; ++j)
-        l += exp(s[j] - m);
+        if (kept(J, h, i, j)) l += exp(s[j] - m);
     /* pass 3: normalised weights a_j, then o = sum_j a_j v_j */
     for (int x = 0; x < d; ++x) o_out[x] = 0.0;
     for (int j = 0; j < nvis; ++j) {
+        if (!kept(J, h, i, j)) continue;
         const double a = exp(s[j] - m) / l;
         const float *vj = J->v + (((int64_t)b * J->Nk + j) * J->Hkv + hk) * d;
         for (int x = 0; x < d; ++x)
@@ -118,19 +137,23 @@ static void *worker(void *arg)
 }
 
 /*
- * oracle_attention: O and LSE for the listed query rows.
+ * oracle_attention_masked: O and LSE for the listed query rows.
  *   q: [B][Nq][Hq][d]; k, v: [B][Nk][Hkv][d].
+ *   mask: NULL, or a block mask [Hq][ceil(Nq/bq)][ceil(Nk/bk)] (bytes, nonzero
+ *         = the block of bq query rows x bk keys is kept).
  *   rows: nrows triples (b, h, i), i < Nq; o: nrows*d doubles; lse: nrows doubles.
  *   scale: applied to q.k (the caller passes the same float the GPU gets).
  *   nthreads: worker threads (>= 1).
  * Returns 0 on success, -1 on a bad argument, -2 on allocation failure.
  */
-int oracle_attention(const float *q, const float *k, const float *v,
-                     int B, int Hq, int Hkv, int Nq, int Nk, int d, double scale,
-                     int causal, const int32_t *rows, int64_t nrows,
-                     double *o, double *lse, int nthreads)
+int oracle_attention_masked(const float *q, const float *k, const float *v,
+                            int B, int Hq, int Hkv, int Nq, int Nk, int d, double scale,
+                            int causal, const uint8_t *mask, int bq, int bk,
+                            const int32_t *rows, int64_t nrows,
+                            double *o, double *lse, int nthreads)
 {
     if (!q || !k || !v || !rows || !o || !lse) return -1;
+    if (mask && (bq < 1 || bk < 1)) return -1;
     if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1 || Hq % Hkv) return -1;
     for (int64_t r = 0; r < nrows; ++r) {
         const int32_t *t = rows + 3 * r;
@@ -142,6 +165,7 @@ int oracle_attention(const float *q, const float *k, const float *v,
     J.q = q; J.k = k; J.v = v;
     J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.Nq = Nq; J.Nk = Nk; J.d = d;
     J.scale = scale; J.causal = causal;
+    J.mask = mask; J.bq = bq; J.bk = bk;
     J.rows = rows; J.nrows = nrows; J.o = o; J.lse = lse;
     J.next = 0;
     pthread_mutex_init(&J.lock, NULL);
@@ -161,6 +185,16 @@ int oracle_attention(const float *q, const float *k, const float *v,
     free(th);
     pthread_mutex_destroy(&J.lock);
     return rc;
+}
+
+/* oracle_attention: oracle_attention_masked without a block mask. */
+int oracle_attention(const float *q, const float *k, const float *v,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int d, double scale,
+                     int causal, const int32_t *rows, int64_t nrows,
+                     double *o, double *lse, int nthreads)
+{
+    return oracle_attention_masked(q, k, v, B, Hq, Hkv, Nq, Nk, d, scale, causal, NULL, 1, 1,
+                                   rows, nrows, o, lse, nthreads);
 }
 
 /* ------------------------------------------------------------------------

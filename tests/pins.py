@@ -406,3 +406,95 @@ def pin_bwd_closed_forms(att, bwd):
 
 
 BWD_PINS = [pin_bwd_closed_forms, pin_bwd_torch_autograd, pin_bwd_finite_differences]
+
+
+# ---------------------------------------------------------- block-sparse mask
+def expand_block_mask(mask, Nq, Nk, bq, bk):
+    """[H, nqb, nkb] block mask -> [H, Nq, Nk] boolean keep-matrix."""
+    m = np.asarray(mask, dtype=bool)
+    return np.repeat(np.repeat(m, bq, axis=1), bk, axis=2)[:, :Nq, :Nk]
+
+
+def pin_block_mask(att):
+    """The block-sparse variant (first page, section 0x04): keys of skipped
+    blocks take no part in a row's softmax."""
+    rng = np.random.default_rng(111)
+    # all-ones mask: identical to the dense result (same arithmetic, same order)
+    B, Hq, Hkv, N, d, bq, bk = 1, 4, 2, 37, 8, 8, 4
+    q, k, v = rand((B, N, Hq, d), 112), rand((B, N, Hkv, d), 113), rand((B, N, Hkv, d), 114)
+    ones = np.ones((Hq, -(-N // bq), -(-N // bk)), np.uint8)
+    for causal in (False, True):
+        a = att(q, k, v, 0.4, causal)
+        b = att(q, k, v, 0.4, causal, block_mask=ones, block=(bq, bk))
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1]), "all-ones mask must equal dense"
+    # one kept key block per query block: equals dense attention over that
+    # slice of K/V; an all-zero mask row gives O = 0 and lse = -inf
+    nqb, nkb = -(-N // bq), -(-N // bk)
+    keep = rng.integers(0, nkb, size=(Hq, nqb))
+    m1 = np.zeros((Hq, nqb, nkb), np.uint8)
+    for h in range(Hq):
+        for a_ in range(nqb):
+            m1[h, a_, keep[h, a_]] = 1
+    m1[1, 2, :] = 0
+    o, l = att(q, k, v, 0.4, False, block_mask=m1, block=(bq, bk))
+    o = o.reshape(B, Hq, N, d)
+    l = l.reshape(B, Hq, N)
+    for h in range(Hq):
+        for i in range(N):
+            if h == 1 and i // bq == 2:
+                assert np.all(o[0, h, i] == 0) and l[0, h, i] == -math.inf, "empty mask row must give zeros"
+                continue
+            c = keep[h, i // bq]
+            sl = slice(c * bk, min(N, (c + 1) * bk))
+            os_, ls_ = att(np.ascontiguousarray(q[:, i:i + 1]), np.ascontiguousarray(k[:, sl]),
+                           np.ascontiguousarray(v[:, sl]), 0.4, False)
+            os_ = os_.reshape(B, Hq, 1, d)
+            assert np.array_equal(o[0, h, i], os_[0, h, 0]), "one kept block must equal attention on that slice"
+            assert l[0, h, i] == ls_.reshape(B, Hq)[0, h], "lse over one kept block"
+    # random masks, causal and not: decimal brute force (tiny) and fp64 sdpa
+    import torch
+    import torch.nn.functional as F
+    for seed, (B, Hq, Hkv, N, d, bq, bk), causal in [
+        (115, (1, 2, 1, 9, 3, 2, 3), True), (116, (2, 2, 2, 7, 2, 4, 2), False),
+    ]:
+        q, k, v = rand((B, N, Hq, d), seed), rand((B, N, Hkv, d), seed + 1), rand((B, N, Hkv, d), seed + 2)
+        m = (np.random.default_rng(seed).random((Hq, -(-N // bq), -(-N // bk))) < 0.6).astype(np.uint8)
+        o, l = att(q, k, v, 0.7, causal, block_mask=m, block=(bq, bk))
+        o, l = o.reshape(B, Hq, N, d), l.reshape(B, Hq, N)
+        keepm = expand_block_mask(m, N, N, bq, bk)
+        if causal:
+            keepm = keepm & np.tril(np.ones((N, N), bool))[None]
+        g = Hq // Hkv
+        getcontext().prec = 40
+        for b in range(B):
+            for h in range(Hq):
+                for i in range(N):
+                    J = [j for j in range(N) if keepm[h, i, j]]
+                    if not J:
+                        assert np.all(o[b, h, i] == 0) and l[b, h, i] == -math.inf
+                        continue
+                    w = [(Decimal(float(np.float32(0.7))) * sum(Decimal(float(q[b, i, h, x])) * Decimal(float(k[b, j, h // g, x]))
+                                                               for x in range(d))).exp() for j in J]
+                    tot = sum(w)
+                    for x in range(d):
+                        ref = float(sum(wj * Decimal(float(v[b, j, h // g, x])) for wj, j in zip(w, J)) / tot)
+                        assert abs(o[b, h, i, x] - ref) < 1e-12, "masked O differs from the decimal brute force"
+                    assert abs(l[b, h, i] - float(tot.ln())) < 1e-12
+    B, Hq, Hkv, N, d, bq, bk = 1, 4, 2, 150, 32, 32, 16
+    q, k, v = rand((B, N, Hq, d), 117), rand((B, N, Hkv, d), 118), rand((B, N, Hkv, d), 119)
+    m = (np.random.default_rng(120).random((Hq, -(-N // bq), -(-N // bk))) < 0.5).astype(np.uint8)
+    m[:, :, 0] = 1                                   # every row keeps a block
+    for causal in (False, True):
+        o, l = att(q, k, v, 0.25, causal, block_mask=m, block=(bq, bk))
+        keepm = torch.from_numpy(expand_block_mask(m, N, N, bq, bk))
+        if causal:
+            keepm = keepm & torch.ones(N, N, dtype=torch.bool).tril()
+        g = Hq // Hkv
+        tq = torch.from_numpy(q).double().permute(0, 2, 1, 3)
+        tk = torch.from_numpy(np.repeat(k, g, axis=2)).double().permute(0, 2, 1, 3)
+        tv = torch.from_numpy(np.repeat(v, g, axis=2)).double().permute(0, 2, 1, 3)
+        ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=keepm[None], scale=float(np.float32(0.25)))
+        assert np.max(np.abs(o.reshape(B, Hq, N, d) - ref.numpy())) < 1e-12, "masked O differs from sdpa"
+
+
+ALL_PINS.append(pin_block_mask)

@@ -31,6 +31,10 @@ MUTATIONS = [
     ("q_from_key_row", "const float *qi = J->q + (((int64_t)b * J->Nq + i)", "const float *qi = J->q + (((int64_t)b * J->Nq + 0)"),
     ("no_normalise", "const double a = exp(s[j] - m) / l;", "const double a = exp(s[j] - m);"),
     ("max_not_subtracted_in_weights", "const double a = exp(s[j] - m) / l;", "const double a = exp(s[j]) / l;"),
+    ("mask_ignored", "if (!J->mask) return 1;", "return 1;"),
+    ("mask_blocks_swapped", "return J->mask[((int64_t)h * nqb + i / J->bq) * nkb + j / J->bk] != 0;",
+     "return J->mask[((int64_t)h * nqb + i / J->bk) * nkb + j / J->bq] != 0;"),
+    ("mask_kv_head", "return J->mask[((int64_t)h * nqb", "return J->mask[((int64_t)(h / (J->Hq / J->Hkv)) * nqb"),
     # backward
     ("bwd_no_softmax_jacobian", "const double ds = p[j] * (dp[j] - pdp);", "const double ds = p[j] * dp[j];"),
     ("bwd_dk_sign", "dkj[x] += J->scale * ds * (double)qi[x];", "dkj[x] -= J->scale * ds * (double)qi[x];"),
