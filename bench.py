@@ -129,14 +129,17 @@ def cpu_baseline(w, seconds: float, hbm: bool):
     threads = oracle.host_threads()
     # calibrate on 1024 evenly strided rows, then size the sample to about
     # `seconds` (every row when the whole workload fits)
+    mk = {}
+    if w.mask:
+        mk = {"block_mask": w.block_mask(), "block": (128, 64)}
     probe = rows[np.linspace(0, len(rows) - 1, min(1024, len(rows))).astype(int)]
     t0 = time.perf_counter()
-    oracle.attention(q, k, v, w.scale, w.causal, rows=probe, threads=threads)
+    oracle.attention(q, k, v, w.scale, w.causal, rows=probe, threads=threads, **mk)
     dt = max(time.perf_counter() - t0, 1e-3)
     n = int(min(len(rows), max(len(probe), len(probe) * seconds / dt)))
     pick = rows[np.linspace(0, len(rows) - 1, n).astype(int)]
     t0 = time.perf_counter()
-    oracle.attention(q, k, v, w.scale, w.causal, rows=pick, threads=threads)
+    oracle.attention(q, k, v, w.scale, w.causal, rows=pick, threads=threads, **mk)
     dt = time.perf_counter() - t0
     sample = (f"all {n} query rows of {w.name}" if n == len(rows) else
               f"{n} of the {len(rows)} query rows of {w.name}, evenly strided over (b, h, i)")
@@ -146,7 +149,12 @@ def cpu_baseline(w, seconds: float, hbm: bool):
         return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
                 "sample": sample + f"; fp64 3-pass oracle, {dt:.1f} s wall; bytes counted as the sample's "
                                    "share of the workload's algorithmic bytes"}
-    vis = visible_keys(w, pick[:, 2])
+    if w.mask:   # kept keys of each sampled row (non-causal block masks)
+        m = mk["block_mask"].numpy().astype(np.float64)
+        keys = np.minimum(w.N - 64 * np.arange(m.shape[2]), 64).astype(np.float64)
+        vis = m[pick[:, 1], pick[:, 2] // 128] @ keys
+    else:
+        vis = visible_keys(w, pick[:, 2])
     flops = float(4.0 * w.d * vis.sum())
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
@@ -245,8 +253,14 @@ def main():
         bws = torch.empty(fa.fa_bwd_workspace_size(w.B, w.Hq, w.N), dtype=torch.uint8, device=dev)
         hbm_bound = False
 
+    sparse = bool(w.mask)
+    if sparse:
+        bmask = w.block_mask().to(dev)
+
     def step():
-        if fp8:
+        if sparse:
+            fa.fwd_blocksparse(q, k, v, bmask, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        elif fp8:
             fa.fwd_fp8(q, k, v, qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
         elif bwd:
             fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=bws,
@@ -292,6 +306,9 @@ def main():
         metric = f"attn bwd TFLOP/s (2.5x forward FLOPs) on {w.name}; % of dense bf16 MFMA peak"
     elif fp8:
         metric = f"attn fwd TFLOP/s on {w.name} (e4m3 inputs, bf16 output); % of dense fp8 MFMA peak"
+    elif sparse:
+        metric = (f"attn fwd TFLOP/s on {w.name} (FLOPs of the kept blocks only); "
+                  "% of dense bf16 MFMA peak")
     else:
         metric = METRIC if headline else (
             f"attn fwd {unit} on {w.name}" + ("; % of HBM peak" if hbm_bound else "; % of dense bf16 MFMA peak"))
@@ -323,6 +340,9 @@ def main():
         out["dtype"] = "bf16" if w.dtype == "bf16" else "f32"
     if bwd:
         out["config"]["pass"] = "bwd"
+    if sparse:
+        out["config"].update({"block_mask": w.mask, "mask_block": [128, 64],
+                              "kept_fraction": round(w.flops / (4.0 * w.B * w.Hq * w.N * w.N * w.d), 4)})
     if fp8:
         out["dtype"] = "fp8-e4m3"
         out["data"] = "synthetic (seeded randn, e4m3 round-to-nearest-even with one scale per (batch, head))"

@@ -29,7 +29,7 @@ import os
 
 from ._build import LIB_PATH
 
-__all__ = ["fwd", "fwd_fp8", "fa_fwd_fp8", "bwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_splitkv_num_splits",
+__all__ = ["fwd", "fwd_blocksparse", "fa_fwd_blocksparse", "fwd_fp8", "fa_fwd_fp8", "bwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_splitkv_num_splits",
            "fa_splitkv_workspace_size", "fa_strerror", "fa_version", "load_library", "FAError",
            "STATUS", "EXPORTS"]
 
@@ -39,7 +39,7 @@ STATUS = {
     "FA_ERR_SPLITS": 9, "FA_ERR_WORKSPACE": 10,
 }
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_splitkv_num_splits",
-           "fa_splitkv_workspace_size", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_size", "fa_strerror",
+           "fa_splitkv_workspace_size", "fa_fwd_blocksparse", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_size", "fa_strerror",
            "fa_version")
 
 _lib = None
@@ -76,6 +76,9 @@ def load_library(path: str = LIB_PATH):
     lib.fa_splitkv_num_splits.argtypes = [ctypes.c_int] * 7
     lib.fa_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.fa_splitkv_workspace_size.argtypes = [ctypes.c_int] * 7
+    lib.fa_fwd_blocksparse.restype = ctypes.c_int
+    lib.fa_fwd_blocksparse.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_void_p])
     lib.fa_fwd_fp8.restype = ctypes.c_int
     lib.fa_fwd_fp8.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
                                ctypes.c_void_p])
@@ -262,6 +265,45 @@ def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal: bool = False, scal
     st = fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(),
                     v_descale.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d, scale, causal,
                     stream.cuda_stream)
+    if st != 0:
+        raise FAError(st, fa_strerror(st))
+    return out, lse
+
+
+MASK_BLOCK = (128, 64)   # query rows x keys per block-mask entry
+
+
+def fa_fwd_blocksparse(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, mask, stream) -> int:
+    return load_library().fa_fwd_blocksparse(q, k, v, o, lse, B, Hq, Hkv, N, d, float(scale), int(causal),
+                                             mask, stream)
+
+
+def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, scale: float | None = None, out=None, lse=None,
+                    stream=None):
+    """Block-sparse bf16 forward.  block_mask: uint8 GPU tensor
+    [Hq, ceil(N/128), ceil(N/64)], nonzero = the block is computed."""
+    import torch
+
+    if not all(t.is_cuda for t in (q, k, v, block_mask)):
+        raise ValueError("fwd_blocksparse: every tensor must be on the GPU (there is no CPU path)")
+    if any(t.dtype != torch.bfloat16 for t in (q, k, v)) or block_mask.dtype != torch.uint8:
+        raise ValueError("fwd_blocksparse: q, k, v bfloat16 and block_mask uint8")
+    if not all(t.is_contiguous() for t in (q, k, v, block_mask)):
+        raise ValueError("fwd_blocksparse: tensors must be contiguous")
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    want = (Hq, -(-N // MASK_BLOCK[0]), -(-N // MASK_BLOCK[1]))
+    if tuple(k.shape) != (B, N, Hkv, d) or v.shape != k.shape or tuple(block_mask.shape) != want:
+        raise ValueError(f"fwd_blocksparse: shape mismatch (mask must be {want})")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = torch.empty_like(q) if out is None else out
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            B, Hq, Hkv, N, d, scale, causal, block_mask.data_ptr(), stream.cuda_stream)
     if st != 0:
         raise FAError(st, fa_strerror(st))
     return out, lse

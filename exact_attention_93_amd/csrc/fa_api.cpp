@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 104;  // 0.1.4
+constexpr int kVersion = 105;  // 0.1.5
 constexpr int kMaxSplits = 256;
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb)
@@ -106,6 +106,8 @@ int validate_and_fill(const void *q, const void *k, const void *v, void *o, floa
     p.o_part = nullptr;
     p.lse_part = nullptr;
     p.q_descale = p.k_descale = p.v_descale = nullptr;
+    p.block_mask = nullptr;
+    p.mask_nqb = p.mask_nkb = 0;
     if (nsplit > 1) {
         const size_t need = workspace_bytes_for(B, Hq, Nq, d, nsplit);
         if (!ws || ws_bytes < need || ((uintptr_t)ws & 15)) return FA_ERR_WORKSPACE;
@@ -146,7 +148,7 @@ int run(const fa::FwdParams &p, int d, bool bf16, hipStream_t stream)
 {
     hipError_t e;
     if (!bf16) e = fa::launch_fwd_f32(p, d, stream);
-    else if (d <= 128 && fa::use_decode(p.Nq, p.group)) e = fa::launch_decode_bf16(p, d, stream);
+    else if (d <= 128 && !p.block_mask && fa::use_decode(p.Nq, p.group)) e = fa::launch_decode_bf16(p, d, stream);
     else e = fa::launch_fwd_bf16(p, d, stream);
     if (e != hipSuccess) return FA_ERR_LAUNCH;
     if (p.nsplit > 1 && fa::launch_combine(p, d, bf16 ? 1 : 0, stream) != hipSuccess) return FA_ERR_LAUNCH;
@@ -211,6 +213,22 @@ size_t fa_splitkv_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, 
     const int nsplit = fa_splitkv_num_splits(B, Hq, Hkv, Nq, Nk, d, num_splits);
     if (nsplit <= 1) return 0;
     return workspace_bytes_for(B, Hq, Nq, d, nsplit);
+}
+
+int fa_fwd_blocksparse(const void *q, const void *k, const void *v, void *o, float *lse,
+                       int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                       const unsigned char *block_mask, void *stream)
+{
+    if (!block_mask) return FA_ERR_NULL;
+    if (N > 65536) return (!q || !k || !v || !o || !lse) ? FA_ERR_NULL : FA_ERR_SHAPE;
+    fa::FwdParams p;
+    const int st = validate_and_fill(q, k, v, o, lse, B, Hq, Hkv, N, N, d, scale, causal, 1,
+                                     nullptr, 0, 2, p, 0, true);
+    if (st != FA_OK) return st;
+    p.block_mask = block_mask;
+    p.mask_nqb = (int)cdiv(N, 128);
+    p.mask_nkb = (int)cdiv(N, 64);
+    return run(p, d, true, (hipStream_t)stream);
 }
 
 int fa_fwd_fp8(const void *q, const void *k, const void *v, const float *q_descale,

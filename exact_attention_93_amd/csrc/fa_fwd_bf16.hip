@@ -154,7 +154,12 @@ __device__ __forceinline__ void lds_wait_vm()
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int D, bool CAUSAL, bool SPLIT>
+// Block-sparse forward: query blocks of kMaskRows rows x key tiles of kBN
+// keys; the workgroup visits only the tiles that one of its query blocks keeps.
+constexpr int kMaskRows = 128;
+constexpr int kMaxMaskTiles = 1024;   // key tiles a block-sparse call may have (N <= 65536)
+
+template <int D, bool CAUSAL, bool SPLIT, bool SPARSE>
 __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams p)
 {
     constexpr int kThreads = wg_threads<D>();
@@ -197,8 +202,49 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     // ---- K/V tiles this workgroup visits: n tiles from key key_lo on
     int kt_lo, kt_hi;
     key_tiles<kBN>(p, q_first, kBM, split, kt_lo, kt_hi);
-    const int n = max(0, kt_hi - kt_lo);
+    int n = max(0, kt_hi - kt_lo);
     const int key_lo = kt_lo * kBN;
+
+    // ---- block-sparse: the tiles any query block of this workgroup keeps,
+    // in order, each with one bit per query block (bit 14 + block)
+    __shared__ uint16_t tile_list[SPARSE ? kMaxMaskTiles : 1];
+    __shared__ int tile_count;
+    if constexpr (SPARSE) {
+        constexpr int QB = kBM / kMaskRows;         // query blocks per workgroup (2, or 1 at d = 256)
+        if (wave == 0) {
+            const int qb0 = q_first / kMaskRows;
+            const int nqb = p.mask_nqb;
+            const uint8_t *mrow = p.block_mask + ((int64_t)h * nqb + qb0) * p.mask_nkb;
+            int cnt = 0;
+            for (int base = kt_lo; base < kt_hi; base += 64) {
+                const int j = base + lane;
+                int bits = 0;
+                if (j < kt_hi) {
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+                        if (qb0 + qb < nqb && mrow[qb * p.mask_nkb + j]) bits |= 1 << qb;
+                }
+                const uint64_t keep = __builtin_amdgcn_ballot_w64(bits != 0);
+                const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(keep >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)keep, 0));
+                if (bits) tile_list[pos] = (uint16_t)(j | (bits << 14));
+                cnt += __builtin_popcountll(keep);
+            }
+            if (lane == 0) tile_count = cnt;
+        }
+        __syncthreads();
+        n = tile_count;
+    }
+    // absolute key-tile index of the loop's j-th tile, and whether this
+    // wavefront's query block keeps it
+    auto tix = [&](int j) -> int {
+        if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane(tile_list[j]) & 0x3fff;
+        else return j;
+    };
+    auto block_keeps = [&](int j) -> bool {
+        if constexpr (SPARSE) return (__builtin_amdgcn_readfirstlane(tile_list[j]) >> (14 + wave * 32 / kMaskRows)) & 1;
+        else return true;
+    };
 
     const int sQ = p.Hq * D, sK = p.Hkv * D;      // row strides (elements)
     const uint16_t *qbase = (const uint16_t *)p.q + ((int64_t)b * Nq * p.Hq + h) * D;
@@ -230,7 +276,9 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     // Tile j holds a key this wavefront can see (causal: keys <= its last
     // row + off).  A wavefront whose rows all lie past the end sees nothing.
     const bool wave_live = wq0 < Nq;
-    auto visible = [&](int j) { return wave_live && (!CAUSAL || key_lo + j * kBN <= wq0 + 31 + off); };
+    auto visible = [&](int j) {
+        return wave_live && (!CAUSAL || key_lo + tix(j) * kBN <= wq0 + 31 + off) && block_keeps(j);
+    };
 
     // ---- HBM -> LDS: each wavefront moves BLKS_PER_WAVE 1 KB blocks of a
     // tile; lane l fills physical chunk l % CHUNKS of row l / CHUNKS.
@@ -240,7 +288,7 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
         for (int i = 0; i < BLKS_PER_WAVE; ++i) {
             const int blk = wave * BLKS_PER_WAVE + i;
             const int row = blk * ROWS_PER_BLK + ld_row;
-            const uint32_t rowoff = (uint32_t)(j * kBN + row) * (uint32_t)(sK * 2);
+            const uint32_t rowoff = (uint32_t)(tix(j) * kBN + row) * (uint32_t)(sK * 2);
             load_lds16(kbase, range, rowoff + ((ld_pch ^ k_swz<D>(row)) * 16), (lds_void_t *)&dst[blk * 512]);
         }
     };
@@ -249,7 +297,7 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
         for (int i = 0; i < BLKS_PER_WAVE; ++i) {
             const int blk = wave * BLKS_PER_WAVE + i;
             const int row = blk * ROWS_PER_BLK + ld_row;
-            const uint32_t rowoff = (uint32_t)(j * kBN + row) * (uint32_t)(sK * 2);
+            const uint32_t rowoff = (uint32_t)(tix(j) * kBN + row) * (uint32_t)(sK * 2);
             load_lds16(vbase, range, rowoff + ((ld_pch ^ v_swz<D>(row)) * 16), (lds_void_t *)&dst[blk * 512]);
         }
     };
@@ -396,9 +444,10 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     // Should a row's scores run more than 64 (base 2) above the reference,
     // its tile sum exceeds 2^64 (or overflows), and that tile is redone with
     // its own maximum and the usual rescale.
+    bool ref_set = false;      // block-sparse: the wavefront has set its reference (uniform)
     auto softmax_step = [&](int j) {
         if (!visible(j)) return;
-        const int key0 = key_lo + j * kBN;
+        const int key0 = key_lo + tix(j) * kBN;
         const bool need_mask = (key0 + kBN > Nk) || (CAUSAL && key0 + kBN - 1 > wq0 + off);
         if (need_mask) {
             const int lim = (CAUSAL ? min(my_q + off, Nk - 1) : Nk - 1) - (key0 + 8 * hf);
@@ -409,7 +458,15 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
                     if (kb * 32 + 16 * (i >> 3) + (i & 7) > lim) sacc[kb][i] = -INFINITY;
         }
         float alpha = 1.f;
-        if (j == 0) alpha = settle(tile_max());
+        // The reference comes from the exact maximum of the wavefront's first
+        // visible tile (tile 0 without a block mask).  Every row that sees
+        // any key sees one there: with a block mask all rows of a wavefront
+        // share the mask row, and a row that the causal rule leaves empty in
+        // that tile sees only larger keys, all masked, in later ones.
+        if (SPARSE ? !ref_set : j == 0) {
+            alpha = settle(tile_max());
+            ref_set = true;
+        }
         float rf = exps();
         if (__builtin_amdgcn_ballot_w64(rf > kFarSum) != 0) {
             alpha *= settle(tile_max());
@@ -507,22 +564,24 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     }
 }
 
-template <int D, bool CAUSAL, bool SPLIT>
+template <int D, bool CAUSAL, bool SPLIT, bool SPARSE>
 hipError_t launch_one(const FwdParams &p_in, hipStream_t stream)
 {
     FwdParams p = p_in;
     p.ntiles = (p.Nq + wg_rows<D>() - 1) / wg_rows<D>();
     const unsigned grid = (unsigned)p.B * (unsigned)p.Hq * (unsigned)p.ntiles * (unsigned)p.nsplit;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPLIT>), dim3(grid), dim3(wg_threads<D>()), 0, stream, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, SPLIT, SPARSE>), dim3(grid), dim3(wg_threads<D>()), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const FwdParams &p, hipStream_t stream)
 {
+    if (p.block_mask)
+        return p.causal ? launch_one<D, true, false, true>(p, stream) : launch_one<D, false, false, true>(p, stream);
     if (p.nsplit > 1)
-        return p.causal ? launch_one<D, true, true>(p, stream) : launch_one<D, false, true>(p, stream);
-    return p.causal ? launch_one<D, true, false>(p, stream) : launch_one<D, false, false>(p, stream);
+        return p.causal ? launch_one<D, true, true, false>(p, stream) : launch_one<D, false, true, false>(p, stream);
+    return p.causal ? launch_one<D, true, false, false>(p, stream) : launch_one<D, false, false, false>(p, stream);
 }
 
 }  // namespace

@@ -32,6 +32,9 @@ struct FwdParams {
     const float *q_descale;   // [B][Hq]
     const float *k_descale;   // [B][Hkv]
     const float *v_descale;   // [B][Hkv]
+    // block-sparse forward: mask [Hq][mask_nqb][mask_nkb] over 128 query rows x 64 keys (NULL: dense)
+    const uint8_t *block_mask;
+    int mask_nqb, mask_nkb;
 };
 
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, hipStream_t stream);

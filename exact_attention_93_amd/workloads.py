@@ -34,6 +34,7 @@ class Workload:
     seed: int
     Nk: int = 0         # key length; 0 = the query length N
     splits: int = 1     # key ranges (0 = the library's choice)
+    mask: str = ""      # block mask pattern ("butterfly"), or dense
 
     @property
     def Nkv(self) -> int:
@@ -63,8 +64,16 @@ class Workload:
 
     @property
     def flops(self) -> float:
-        """4*d FLOPs per credited (query, key) pair per head and batch entry."""
+        """4*d FLOPs per credited (query, key) pair per head and batch entry
+        (with a block mask: the pairs it keeps)."""
+        if self.mask:
+            return 4.0 * self.B * self.d * mask_kept_pairs(self.block_mask(), self.N, self.causal)
         return 4.0 * self.B * self.Hq * self.pairs * self.d
+
+    def block_mask(self):
+        if self.mask == "butterfly":
+            return butterfly_mask(self.Hq, self.N)
+        raise ValueError(self.mask)
 
     @property
     def io_bytes(self) -> int:
@@ -110,7 +119,47 @@ D256_WORKLOADS = {
     "causal_bf16_B2_H16_N4096_d256": Workload(
         "causal_bf16_B2_H16_N4096_d256", 2, 16, 16, 4096, 256, "bf16", True, 1.0, 1009),
 }
-ALL_WORKLOADS = {**WORKLOADS, **SPLIT_WORKLOADS, **FP8_WORKLOADS, **D256_WORKLOADS}
+# Block-sparse: a butterfly pattern over 128 x 128 blocks (the sparsity form
+# the first page names for block-sparse FlashAttention): block row a keeps
+# key block c iff a == c or a xor c is a power of two; 8 of 128 blocks at
+# N = 16384, the FLOPs of the headline case.
+SPARSE_WORKLOADS = {
+    "butterfly_bf16_B1_H32_N16384_d128": Workload(
+        "butterfly_bf16_B1_H32_N16384_d128", 1, 32, 32, 16384, 128, "bf16", False, 1.0, 1010, mask="butterfly"),
+}
+ALL_WORKLOADS = {**WORKLOADS, **SPLIT_WORKLOADS, **FP8_WORKLOADS, **D256_WORKLOADS, **SPARSE_WORKLOADS}
+MASK_BLOCK = (128, 64)      # query rows x keys per block-mask entry of the GPU library
+
+
+def butterfly_mask(Hq: int, N: int) -> torch.Tensor:
+    """uint8 block mask [Hq, ceil(N/128), ceil(N/64)] of the butterfly pattern
+    over 128 x 128 blocks (each 128-key block is two 64-key mask columns)."""
+    nb = -(-N // 128)
+    a = torch.arange(nb)[:, None]
+    c = torch.arange(nb)[None, :]
+    x = a ^ c
+    keep = (x == 0) | ((x & (x - 1)) == 0)
+    m = keep.repeat_interleave(2, dim=1)[:, : -(-N // 64)]
+    return m.to(torch.uint8).unsqueeze(0).expand(Hq, -1, -1).contiguous()
+
+
+def random_block_mask(Hq: int, N: int, density: float, seed: int) -> torch.Tensor:
+    """uint8 block mask [Hq, ceil(N/128), ceil(N/64)] with entries kept with
+    probability `density` (seeded)."""
+    g = torch.Generator().manual_seed(seed)
+    shape = (Hq, -(-N // 128), -(-N // 64))
+    return (torch.rand(shape, generator=g) < density).to(torch.uint8).contiguous()
+
+
+def mask_kept_pairs(mask: torch.Tensor, N: int, causal: bool) -> float:
+    """(query, key) pairs a block mask keeps, summed over heads (causal rule included)."""
+    if not causal:   # block extents times kept entries
+        rows = torch.clamp(N - 128 * torch.arange(mask.shape[1]), max=128).to(torch.float64)
+        keys = torch.clamp(N - 64 * torch.arange(mask.shape[2]), max=64).to(torch.float64)
+        return float((mask.to(torch.float64) * rows[None, :, None] * keys[None, None, :]).sum())
+    m = mask.to(torch.bool).repeat_interleave(128, dim=1)[:, :N].repeat_interleave(64, dim=2)[:, :, :N]
+    m = m & torch.ones(N, N, dtype=torch.bool).tril()
+    return float(m.sum())
 
 
 def make(B, Hq, Hkv, N, d, dtype="bf16", causal=False, q_std=1.0, seed=0, name="custom", Nk=0,

@@ -147,6 +147,22 @@ int fa_splitkv_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num
 size_t fa_splitkv_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
 
 /*
+ * fa_fwd_blocksparse -- fa_fwd restricted to the blocks a block mask keeps:
+ * the block-sparse variant of the first page's section 0x04, where blocks
+ * of the score matrix that a sparsity pattern marks are skipped entirely.
+ *   block_mask : device bytes [Hq][ceil(N/128)][ceil(N/64)]; entry [h][a][c]
+ *                nonzero keeps keys 64c .. 64c+63 for query rows
+ *                128a .. 128a+127 of head h (together with the causal rule).
+ * Each row's softmax runs over its kept keys alone; a row that keeps none
+ * gets O = 0 and lse = -inf.  Skipped blocks cost no memory traffic and no
+ * arithmetic.  bf16 as fa_fwd; d in {64, 128, 256}; N <= 65536.  Other
+ * arguments, errors and limits as for fa_fwd; FA_ERR_NULL for a NULL mask.
+ */
+int fa_fwd_blocksparse(const void *q, const void *k, const void *v, void *o, float *lse,
+                       int B, int Hq, int Hkv, int N, int d, float scale, int causal,
+                       const unsigned char *block_mask, void *stream);
+
+/*
  * fa_fwd_fp8 -- the forward with fp8 inputs: the low-precision path of the
  * second page's section 10 (FlashAttention-3 FP8) with per-block scales
  * (section 12.2), one block per (batch, head).

@@ -29,7 +29,8 @@ def gpu_fwd(q, k, v, causal, scale, num_splits=1):
     return o.cpu(), lse.cpu()
 
 
-def compare(q, k, v, causal, scale, o, lse, rows=None, kind=None, label="", exact_bounds=False):
+def compare(q, k, v, causal, scale, o, lse, rows=None, kind=None, label="", exact_bounds=False,
+            block_mask=None):
     """Compare GPU outputs o [B,N,Hq,d], lse [B,Hq,N] with the oracle on rows.
 
     exact_bounds=True applies the stated bounds verbatim (the named
@@ -38,7 +39,10 @@ def compare(q, k, v, causal, scale, o, lse, rows=None, kind=None, label="", exac
     rounding error, ulp(ref)/4, on top of 1e-3.
     """
     kind = kind or ("fp32" if q.dtype == torch.float32 else "bf16")
-    ro, rl = oracle.attention(q, k, v, scale, causal, rows=rows)
+    if block_mask is None:
+        ro, rl = oracle.attention(q, k, v, scale, causal, rows=rows)
+    else:   # 128 query rows x 64 keys per mask entry, as the GPU library reads it
+        ro, rl = oracle.attention(q, k, v, scale, causal, rows=rows, block_mask=block_mask, block=(128, 64))
     B, N, Hq, d = q.shape
     if rows is None:
         go = o.float().numpy().transpose(0, 2, 1, 3).reshape(-1, d).astype(np.float64)
@@ -66,7 +70,7 @@ def compare(q, k, v, causal, scale, o, lse, rows=None, kind=None, label="", exac
         # Off the unit-variance workload the fp32 rounding of the scores
         # themselves can exceed 1e-5 (peaked logits): the bound becomes twice
         # the error of a plain fp32 evaluation of the same definition.
-        pe = plain_fp32_error(q, k, v, causal, scale, ro, rows)
+        pe = plain_fp32_error(q, k, v, causal, scale, ro, rows, block_mask)
         tmax, tmean = max(tmax, 2 * pe[0]), max(tmean, 2 * pe[1])
         say(f"[parity] {label}: plain fp32 evaluation error max {pe[0]:.3e} mean {pe[1]:.3e}")
     assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl)), "non-finite output"
@@ -89,7 +93,7 @@ def compare(q, k, v, causal, scale, o, lse, rows=None, kind=None, label="", exac
     return mx, mean, lmx
 
 
-def plain_fp32_error(q, k, v, causal, scale, ro, rows):
+def plain_fp32_error(q, k, v, causal, scale, ro, rows, block_mask=None):
     """Error of softmax(scale Q K^T) V evaluated in float32 on the CPU (torch),
     against the fp64 oracle values ro; (max, mean)."""
     B, N, Hq, d = q.shape
@@ -101,6 +105,10 @@ def plain_fp32_error(q, k, v, causal, scale, ro, rows):
     s = torch.matmul(qt, kt) * np.float32(scale)
     if causal:   # bottom-right alignment: key j kept iff j - i <= Nk - N
         s = s.masked_fill(~torch.ones(N, Nk, dtype=torch.bool).tril(Nk - N), float("-inf"))
+    if block_mask is not None:
+        keep = torch.as_tensor(block_mask).to(torch.bool).repeat_interleave(128, dim=1)[:, :N]
+        keep = keep.repeat_interleave(64, dim=2)[:, :, :Nk]
+        s = s.masked_fill(~keep[None], float("-inf"))
     o = torch.nan_to_num(torch.matmul(torch.softmax(s, dim=-1), vt), nan=0.0)   # [B, Hq, N, d]
     if rows is None:
         o = o.reshape(-1, d)

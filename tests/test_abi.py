@@ -46,7 +46,7 @@ def test_status_codes_match_header():
 
 
 def test_version_and_strerror(lib):
-    assert fa.fa_version() == 104
+    assert fa.fa_version() == 105
     for st in range(11):
         assert fa.fa_strerror(st)
     assert "unknown" in fa.fa_strerror(99)
@@ -206,3 +206,21 @@ def test_invalid_arguments_fp8(lib):
     assert fcall(Hq=3) == S["FA_ERR_HEADS"]
     assert fcall(scale=float("nan")) == S["FA_ERR_SCALE"]
     assert fcall(o=Q + 1024) == S["FA_ERR_ALIAS"]      # bf16 output running over the fp8 q
+
+
+def test_invalid_arguments_blocksparse(lib):
+    S = fa.STATUS
+    MK = 0xC0000000
+
+    def mcall(q=Q, k=K, v=V, o=O, lse=L, mask=MK, **kw):
+        a = dict(B=1, Hq=4, Hkv=2, N=300, d=128, scale=0.1, causal=1)
+        a.update(kw)
+        return fa.fa_fwd_blocksparse(q, k, v, o, lse, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["scale"],
+                                     a["causal"], mask, None)
+    assert mcall(mask=None) == S["FA_ERR_NULL"]
+    assert mcall(q=None) == S["FA_ERR_NULL"]
+    assert mcall(N=65537) == S["FA_ERR_SHAPE"]
+    assert mcall(d=96) == S["FA_ERR_HEADDIM"]
+    assert mcall(Hq=3) == S["FA_ERR_HEADS"]
+    assert mcall(o=O + 2) == S["FA_ERR_ALIGN"]
+    assert mcall(lse=Q) == S["FA_ERR_ALIAS"]
