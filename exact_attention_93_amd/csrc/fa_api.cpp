@@ -251,7 +251,7 @@ int fa_fwd_fp8(const void *q, const void *k, const void *v, const float *q_desca
 size_t fa_bwd_workspace_size(int B, int Hq, int Nq)
 {
     if (B < 1 || Hq < 1 || Nq < 1) return 0;
-    return (size_t)B * Hq * Nq * sizeof(float);
+    return 2 * (size_t)B * Hq * Nq * sizeof(float);   // delta, then lse in base 2
 }
 
 int fa_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse,
@@ -289,6 +289,7 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
     fa::BwdParams p;
     p.q = q; p.k = k; p.v = v; p.o = o; p.dout = dout; p.lse = lse;
     p.delta = (float *)workspace;
+    p.lse2 = (float *)workspace + (size_t)B * Hq * Nq;
     p.dq = dq; p.dk = dk; p.dv = dv;
     p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk;
     p.off = Nk - Nq;

@@ -39,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -193,7 +195,10 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p)
         for (int t = 0; t < KSTEPS; ++t) qreg[t] = doreg[t] = u32x4_t{0, 0, 0, 0};
     }
     delta = sum_halves(delta);
-    if (hf == 0 && my_q < Nq) p.delta[((int64_t)b * p.Hq + h) * Nq + my_q] = delta;
+    if (hf == 0 && my_q < Nq) {
+        p.delta[((int64_t)b * p.Hq + h) * Nq + my_q] = delta;
+        p.lse2[((int64_t)b * p.Hq + h) * Nq + my_q] = lse2;   // for the dK/dV kernel
+    }
     if (p.qmode != 0) {
         const uint32_t keep = p.qmode == 2 ? 0u : 0xffffffffu;
         const uint32_t flip = p.qmode == 1 ? 0x80008000u : 0u;
@@ -395,7 +400,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p)
         if (wave == 0) {                  // the tile's 64 lse and delta values
             const int64_t r0 = ((int64_t)b * p.Hq + h) * Nq;
             const int rng = max(0, Nq - qt * BQ) * 4;
-            load_lds4(p.lse + r0 + qt * BQ, rng, lane * 4, (lds_void_t *)ld);
+            load_lds4(p.lse2 + r0 + qt * BQ, rng, lane * 4, (lds_void_t *)ld);
             load_lds4(p.delta + r0 + qt * BQ, rng, lane * 4, (lds_void_t *)dd);
         }
     };
@@ -407,7 +412,78 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p)
         for (int i = 0; i < 16; ++i) dk[xb][i] = dv[xb][i] = 0.f;
     const int prow = perm_row(lk);
 
-    auto compute = [&](int it, const uint16_t *qs_, const uint16_t *os_, const float *ls, const float *dsm) {
+    // One query tile (two 32-row blocks) in one basic block, in the order
+    //   S0, dP0 | softmax 0 | S1, dP1 | dV0, dK0 | softmax 1 | dV1, dK1,
+    // so that the compiler can run each softmax (vector ALU) under the
+    // neighbouring independent products (one wavefront per SIMD: overlap
+    // comes from within the wavefront).  The masked form (tiles that cross
+    // the diagonal or the end) is a separate instance.
+    auto sdp_products = [&](int qb, const char *qs, const char *os, f32x16_t &s, f32x16_t &dp)
+                            __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+            s = mfma_bf16(row_chunk<D>(qs, qb * 32 + prow, 2 * t + hf), kreg[t], s);
+            dp = mfma_bf16(row_chunk<D>(os, qb * 32 + prow, 2 * t + hf), vreg[t], dp);
+        }
+    };
+    // register i holds query row qt*BQ + qb*32 + 16*(i/8) + 8*hf + (i%8)
+    auto softmax = [&](auto masked, int qt, int qb, const f32x16_t &s, const f32x16_t &dp, const float *ls,
+                       const float *dsm, u32x4_t (&pb)[2], u32x4_t (&dsb)[2]) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(masked)::value;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int lq0 = qb * 32 + 16 * u + 8 * hf;   // first of the 8 rows in LDS order
+            const f32x4_t la = *(const f32x4_t *)&ls[lq0], lb = *(const f32x4_t *)&ls[lq0 + 4];
+            const f32x4_t da = *(const f32x4_t *)&dsm[lq0], db = *(const f32x4_t *)&dsm[lq0 + 4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                float pv[2], dsv[2];
+#pragma unroll
+                for (int z = 0; z < 2; ++z) {
+                    const int e = 2 * w + z, i = 8 * u + e;
+                    const float l2 = e < 4 ? la[e] : lb[e - 4];
+                    const float dr = e < 4 ? da[e] : db[e - 4];
+                    float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -l2));
+                    if (MASK) {
+                        const int qi = qt * BQ + qb * 32 + 16 * u + 8 * hf + e;
+                        if (qi >= Nq || (CAUSAL && my_k > qi + off)) pe = 0.f;
+                    }
+                    pv[z] = pe;
+                    dsv[z] = pe * (dp[i] - dr);
+                }
+                pb[u][w] = pack_bf16(pv[0], pv[1]);
+                dsb[u][w] = pack_bf16(dsv[0], dsv[1]);
+            }
+        }
+    };
+    auto dvdk_products = [&](int qb, const char *qs, const char *os, const u32x4_t (&pb)[2],
+                             const u32x4_t (&dsb)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int xb = 0; xb < XB; ++xb) {
+                dv[xb] = mfma_bf16(tr_operand<D>(os + qb * 32 * ROW_BYTES, u, xb, lane), pb[u], dv[xb]);
+                dk[xb] = mfma_bf16(tr_operand<D>(qs + qb * 32 * ROW_BYTES, u, xb, lane), dsb[u], dk[xb]);
+            }
+    };
+    auto tile_compute = [&](auto masked, int qt, const char *qs, const char *os, const float *ls, const float *dsm)
+                            __attribute__((always_inline)) {
+        static_assert(NQB == 2, "two 32-row blocks per query tile");
+        f32x16_t s0, dp0, s1, dp1;
+        u32x4_t pb0[2], dsb0[2], pb1[2], dsb1[2];
+        sdp_products(0, qs, os, s0, dp0);
+        softmax(masked, qt, 0, s0, dp0, ls, dsm, pb0, dsb0);
+        sdp_products(1, qs, os, s1, dp1);
+        dvdk_products(0, qs, os, pb0, dsb0);
+        softmax(masked, qt, 1, s1, dp1, ls, dsm, pb1, dsb1);
+        dvdk_products(1, qs, os, pb1, dsb1);
+    };
+    // Non-causal: one 32-row block at a time (the per-tile form below makes
+    // the compiler spill at d = 128 without a causal mask).
+    auto compute_blockwise = [&](int it, const uint16_t *qs_, const uint16_t *os_, const float *ls, const float *dsm)
+                                 __attribute__((always_inline)) {
         const int qt = qt_lo + (it - (it / nqt) * nqt);
         const char *qs = (const char *)qs_, *os = (const char *)os_;
 #pragma unroll
@@ -439,7 +515,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p)
                         const int e = 2 * w + z, i = 8 * u + e;
                         const float lr = e < 4 ? la[e] : lb[e - 4];
                         const float dr = e < 4 ? da[e] : db[e - 4];
-                        const float l2 = lr == -INFINITY ? INFINITY : lr * kLog2e;
+                        const float l2 = lr;   // already lse * log2(e), +inf for rows without keys
                         float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -l2));
                         if (need_mask) {
                             const int qi = qrow0 + 16 * u + 8 * hf + e;
@@ -462,17 +538,33 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p)
         }
     };
 
+    auto compute = [&](int it, const uint16_t *qs_, const uint16_t *os_, const float *ls, const float *dsm)
+                       __attribute__((always_inline)) {
+        const int qt = qt_lo + (it - (it / nqt) * nqt);
+        const int qrow0 = qt * BQ;
+        // some (row, key) pair of this wavefront is masked: a row past the
+        // end, or (causal) the tile's first row sees fewer than all keys
+        const bool need_mask = (qrow0 + BQ > Nq) || (CAUSAL && qrow0 + off < wk0 + 31);
+        if (need_mask) tile_compute(std::true_type{}, qt, (const char *)qs_, (const char *)os_, ls, dsm);
+        else tile_compute(std::false_type{}, qt, (const char *)qs_, (const char *)os_, ls, dsm);
+    };
+    auto step = [&](int it, const uint16_t *qs_, const uint16_t *os_, const float *ls, const float *dsm)
+                    __attribute__((always_inline)) {
+        if constexpr (CAUSAL) compute(it, qs_, os_, ls, dsm);
+        else compute_blockwise(it, qs_, os_, ls, dsm);
+    };
+
     if (total > 0) load(0, Qs0, Os0, Ls0, Ds0);
     for (int it = 0; it < total; it += 2) {
         vm_wait_all();
         __syncthreads();
         if (it + 1 < total) load(it + 1, Qs1, Os1, Ls1, Ds1);
-        if (wave_live) compute(it, Qs0, Os0, Ls0, Ds0);
+        if (wave_live) step(it, Qs0, Os0, Ls0, Ds0);
         if (it + 1 < total) {
             vm_wait_all();
             __syncthreads();
             if (it + 2 < total) load(it + 2, Qs0, Os0, Ls0, Ds0);
-            if (wave_live) compute(it + 1, Qs1, Os1, Ls1, Ds1);
+            if (wave_live) step(it + 1, Qs1, Os1, Ls1, Ds1);
         }
     }
 

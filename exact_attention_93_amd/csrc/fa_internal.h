@@ -52,6 +52,7 @@ struct BwdParams {
     const void *q, *k, *v, *o, *dout;   // bf16 inputs (o: the forward's output)
     const float *lse;                   // the forward's log-sum-exp [B][Hq][Nq]
     float *delta;                       // workspace: rowsum(dO * O) [B][Hq][Nq]
+    float *lse2;                        // workspace: lse * log2(e), +inf for rows without keys [B][Hq][Nq]
     void *dq, *dk, *dv;                 // bf16 outputs
     int B, Hq, Hkv, Nq, Nk;
     int off;                            // Nk - Nq (bottom-right causal alignment)
