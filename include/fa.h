@@ -201,7 +201,7 @@ int fa_fwd_fp8(const void *q, const void *k, const void *v, const float *q_desca
  *   scale, causal  : as passed to the forward;
  *   workspace      : at least fa_bwd_workspace_size(B, Hq, Nq) bytes of device
  *                    memory, 4-byte aligned, owned by the caller; overwritten
- *                    (it receives delta).
+ *                    (it receives delta and lse * log2(e) per row).
  * dq, dk, dv are fully written, rounded to nearest even.  Two kernels are
  * enqueued on `stream`: dq (query-block outer, also writing delta) and then
  * dk, dv (key-block outer).  The result is deterministic (no atomics).
@@ -214,7 +214,8 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
            int Nq, int Nk, int d, float scale, int causal, void *workspace,
            size_t workspace_bytes, void *stream);
 
-/* Workspace bytes fa_bwd needs: B * Hq * Nq * 4 (0 for invalid sizes). */
+/* Workspace bytes fa_bwd needs: 2 * B * Hq * Nq * 4 (the rows' delta and
+ * lse in base 2; 0 for invalid sizes). */
 size_t fa_bwd_workspace_size(int B, int Hq, int Nq);
 
 /* Human-readable text for an fa_status value (static storage, never NULL). */

@@ -184,7 +184,7 @@ def test_invalid_arguments_bwd(lib):
     assert bcall(dq=Q) == S["FA_ERR_ALIAS"]
     assert bcall(dv=0x90000000 + 64) == S["FA_ERR_ALIAS"]       # dv overlaps dk
     assert bcall(ws=L) == S["FA_ERR_ALIAS"]                      # workspace on lse
-    assert fa.fa_bwd_workspace_size(2, 4, 16) == 2 * 4 * 16 * 4
+    assert fa.fa_bwd_workspace_size(2, 4, 16) == 2 * (2 * 4 * 16 * 4)   # delta and lse in base 2
     assert fa.fa_bwd_workspace_size(0, 4, 16) == 0
 
 
