@@ -57,24 +57,33 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(FwdParams p, int spl)
     __shared__ float red_w[kThreads / 16];
     __shared__ __attribute__((aligned(16))) f32x4_t red_o[kThreads];
 
-    // this group's ranges, merged against their running maximum m
+    // this group's ranges, four at a time: the loads of a batch are issued
+    // together (a range index past the end is clamped and weighted 0), then
+    // merged against the running maximum m without branches.  An empty range
+    // (L_r = -inf) gets weight 0, and while every range so far was empty
+    // (m = -inf) nothing is rescaled.
     float m = -INFINITY, wsum = 0.f;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     if (live) {
-#pragma unroll 4
-        for (int r = sl; r < p.nsplit; r += spl) {
-            const float lr = p.lse_part[r * rows + row];
-            const f32x4_t o = *(const f32x4_t *)(p.o_part + (r * rows + row) * D + x);
-            if (lr == -INFINITY) continue;
-            if (lr > m) {
-                const float a = expf(m - lr);                  // 0 while m is -inf
-                acc *= a;
-                wsum *= a;
-                m = lr;
+        for (int r0 = sl; r0 < p.nsplit; r0 += 4 * spl) {
+            float lr[4];
+            f32x4_t o[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int r = min(r0 + k * spl, p.nsplit - 1);
+                lr[k] = p.lse_part[r * rows + row];
+                o[k] = *(const f32x4_t *)(p.o_part + (r * rows + row) * D + x);
             }
-            const float w = expf(lr - m);
-            wsum += w;
-            acc += w * o;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float l = r0 + k * spl < p.nsplit ? lr[k] : -INFINITY;
+                const float m_new = fmaxf(m, l);
+                const float a = m_new == -INFINITY ? 1.f : expf(m - m_new);   // 0 when m is -inf
+                const float w = l == -INFINITY ? 0.f : expf(l - m_new);
+                acc = acc * a + w * o[k];
+                wsum = wsum * a + w;
+                m = m_new;
+            }
         }
     }
     red_o[tid] = acc;
