@@ -154,6 +154,15 @@ __device__ __forceinline__ void lds_wait_vm()
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Workgroup barrier that leaves this wavefront's global-to-LDS loads in
+// flight (__syncthreads() would wait for them): only its LDS accesses
+// complete first.  One asm statement with a memory clobber, so no LDS access
+// moves across it.
+__device__ __forceinline__ void barrier_keep_loads()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // Block-sparse forward: query blocks of kMaskRows rows x key tiles of kBN
 // keys; the workgroup visits only the tiles that one of its query blocks keeps.
 constexpr int kMaskRows = 128;
@@ -512,8 +521,12 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
                 softmax_step(s >> 1);
             }
         }
-        if (t & 1) lds_wait_vm();            // K_{j+1}, V_j resident before phase 2j+2
-        __syncthreads();
+        if (t & 1) {                         // K_{j+1}, V_j resident before phase 2j+2
+            lds_wait_vm();
+            __syncthreads();
+        } else {                             // they may still be arriving
+            barrier_keep_loads();
+        }
     };
     for (int t = 0; t < nphase; t += 4) {
         // even j = t/2: K_j in Ks0, V_{j-1} in Vs1; loads go to Ks1, Vs0
