@@ -103,6 +103,15 @@ __device__ __forceinline__ void lds_wait_vm()
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Workgroup barrier that leaves this wavefront's global-to-LDS loads in
+// flight (__syncthreads() would wait for them): only its LDS accesses
+// complete first.  One asm statement with a memory clobber, so no LDS access
+// moves across it.
+__device__ __forceinline__ void barrier_keep_loads()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 1) fwd_fp8_kernel(FwdParams p)
 {
@@ -301,8 +310,12 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_fp8_kernel(FwdParams p)
                 softmax_step(s >> 1);
             }
         }
-        if (t & 1) lds_wait_vm();
-        __syncthreads();
+        if (t & 1) {                         // the next tiles resident before the next even phase
+            lds_wait_vm();
+            __syncthreads();
+        } else {                             // they may still be arriving
+            barrier_keep_loads();
+        }
     };
     for (int t = 0; t < nphase; t += 4) {
         phase(t, Ks0, Vs1, Ks1, Vs0);
