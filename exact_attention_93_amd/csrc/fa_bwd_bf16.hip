@@ -91,10 +91,12 @@ template <int D> __device__ __forceinline__ int swz(int row)
     return D == 128 ? (4 * (row & 3) | ((row >> 2) & 3)) : (4 * ((row >> 1) & 1) | ((row >> 2) & 3));
 }
 
-__device__ __forceinline__ void load_lds16(const void *base, int range, uint32_t off, lds_void_t *dst)
+// 16 bytes per lane from base + soff + voff (bytes) into LDS at dst + 16*lane;
+// soff is the wavefront-uniform part of the offset.
+__device__ __forceinline__ void load_lds16(const void *base, int range, uint32_t voff, uint32_t soff, lds_void_t *dst)
 {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, range, 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, soff, 0, 0);
 }
 __device__ __forceinline__ void load_lds4(const void *base, int range, uint32_t off, lds_void_t *dst)
 {
@@ -220,15 +222,23 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p)
     const uint16_t *kbase = (const uint16_t *)p.k + ((int64_t)b * Nk * p.Hkv + hk) * D;
     const uint16_t *vbase = (const uint16_t *)p.v + ((int64_t)b * Nk * p.Hkv + hk) * D;
     const int range = Nk * sK * 2;
+    // Per-lane byte offsets within a tile are fixed; the tile's own offset
+    // goes in as the scalar offset, and the LDS destinations are uniform.
     const int ld_row = lane / CHUNKS, ld_pch = lane % CHUNKS;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t ld_voff[BLKS_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < BLKS_PER_WAVE; ++i) {
+        const int row = (wave * BLKS_PER_WAVE + i) * ROWS_PER_BLK + ld_row;
+        ld_voff[i] = (uint32_t)row * (uint32_t)(sK * 2) + ((ld_pch ^ swz<D>(row)) * 16);
+    }
     auto load = [&](int j, uint16_t *kd, uint16_t *vd) {
+        const uint32_t soff = (uint32_t)(j * BN) * (uint32_t)(sK * 2);
 #pragma unroll
         for (int i = 0; i < BLKS_PER_WAVE; ++i) {
-            const int blk = wave * BLKS_PER_WAVE + i;
-            const int row = blk * ROWS_PER_BLK + ld_row;
-            const uint32_t o = (uint32_t)(j * BN + row) * (uint32_t)(sK * 2) + ((ld_pch ^ swz<D>(row)) * 16);
-            load_lds16(kbase, range, o, (lds_void_t *)&kd[blk * 512]);
-            load_lds16(vbase, range, o, (lds_void_t *)&vd[blk * 512]);
+            const int blk = wave_u * BLKS_PER_WAVE + i;
+            load_lds16(kbase, range, ld_voff[i], soff, (lds_void_t *)&kd[blk * 512]);
+            load_lds16(vbase, range, ld_voff[i], soff, (lds_void_t *)&vd[blk * 512]);
         }
     };
 
@@ -238,6 +248,39 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p)
 #pragma unroll
         for (int i = 0; i < 16; ++i) dqacc[xb][i] = 0.f;
     const int prow = perm_row(lq);
+    // LDS read addresses.  The chunk permutation depends on a row only
+    // through bits that every row a lane reads shares, so the row reads of
+    // K and V (rows kb*32 + prow) derive from KSTEPS per-lane offsets and the
+    // transposed reads of K (rows 16u + 4r + tr_row) from 2*XB, plus
+    // constant row offsets.
+    int rc_off[KSTEPS], tr_off[2][XB];
+    {
+        const int tg = lane >> 4, ts = lane & 15;
+        const int tr_row = 8 * (tg >> 1) + (ts >> 2);
+        const int tr_chunk = 2 * (tg & 1) + ((ts & 3) >> 1);
+        const int tr_byte = 8 * (ts & 1);
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) rc_off[t] = prow * (D * 2) + (((2 * t + hf) ^ swz<D>(prow)) * 16);
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int xb = 0; xb < XB; ++xb) {
+                const int rw = 4 * r + tr_row;
+                tr_off[r][xb] = rw * (D * 2) + (((4 * xb + tr_chunk) ^ swz<D>(rw)) * 16) + tr_byte;
+            }
+    }
+    // transposed operand A[x][k] = tile[16u + k][32xb + x] (as tr_operand)
+    auto tr_read = [&](const char *tile, int u, int xb) __attribute__((always_inline)) -> u32x4_t {
+        u32x4_t a;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const i16x4_t t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(tile + tr_off[r][xb] + 16 * u * (D * 2)));
+            const u32x2_t t2 = __builtin_bit_cast(u32x2_t, t4);
+            a[2 * r] = t2[0];
+            a[2 * r + 1] = t2[1];
+        }
+        return a;
+    };
 
     // One 32-key half of the tile at a time: S^T and dP^T for those keys,
     // dS^T in bf16, then its share of dQ^T += K^T dS^T.
@@ -251,11 +294,11 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p)
             f32x16_t s, dp;
 #pragma unroll
             for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
-            const int row = kb * 32 + prow;
 #pragma unroll
             for (int t = 0; t < KSTEPS; ++t) {
-                s = mfma_bf16(row_chunk<D>(ks, row, 2 * t + hf), qreg[t], s);
-                dp = mfma_bf16(row_chunk<D>(vs, row, 2 * t + hf), doreg[t], dp);
+                const int o = rc_off[t] + kb * 32 * (D * 2);
+                s = mfma_bf16(*(const u32x4_t *)(ks + o), qreg[t], s);
+                dp = mfma_bf16(*(const u32x4_t *)(vs + o), doreg[t], dp);
             }
             u32x4_t dsb[2];
 #pragma unroll
@@ -276,7 +319,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p)
             for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int xb = 0; xb < XB; ++xb)
-                    dqacc[xb] = mfma_bf16(tr_operand<D>(ks, 2 * kb + u, xb, lane), dsb[u], dqacc[xb]);
+                    dqacc[xb] = mfma_bf16(tr_read(ks, 2 * kb + u, xb), dsb[u], dqacc[xb]);
         }
     };
 
@@ -383,19 +426,27 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p)
     const bool wave_live = wk0 < Nk;
 
     const int range = Nq * sQ * 2;
+    // Per-lane byte offsets within a tile are fixed; the tile's own offset
+    // goes in as the scalar offset, and the LDS destinations are uniform.
     const int ld_row = lane / CHUNKS, ld_pch = lane % CHUNKS;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t ld_voff[BLKS_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < BLKS_PER_WAVE; ++i) {
+        const int row = (wave * BLKS_PER_WAVE + i) * ROWS_PER_BLK + ld_row;
+        ld_voff[i] = (uint32_t)row * (uint32_t)(sQ * 2) + ((ld_pch ^ swz<D>(row)) * 16);
+    }
     auto load = [&](int it, uint16_t *qd, uint16_t *od, float *ld, float *dd) {
         const int hh = it / nqt, qt = qt_lo + (it - (it / nqt) * nqt);
         const int h = hk * G + hh;
         const uint16_t *qb = (const uint16_t *)p.q + ((int64_t)b * Nq * p.Hq + h) * D;
         const uint16_t *ob = (const uint16_t *)p.dout + ((int64_t)b * Nq * p.Hq + h) * D;
+        const uint32_t soff = (uint32_t)(qt * BQ) * (uint32_t)(sQ * 2);
 #pragma unroll
         for (int i = 0; i < BLKS_PER_WAVE; ++i) {
-            const int blk = wave * BLKS_PER_WAVE + i;
-            const int row = blk * ROWS_PER_BLK + ld_row;
-            const uint32_t o = (uint32_t)(qt * BQ + row) * (uint32_t)(sQ * 2) + ((ld_pch ^ swz<D>(row)) * 16);
-            load_lds16(qb, range, o, (lds_void_t *)&qd[blk * 512]);
-            load_lds16(ob, range, o, (lds_void_t *)&od[blk * 512]);
+            const int blk = wave_u * BLKS_PER_WAVE + i;
+            load_lds16(qb, range, ld_voff[i], soff, (lds_void_t *)&qd[blk * 512]);
+            load_lds16(ob, range, ld_voff[i], soff, (lds_void_t *)&od[blk * 512]);
         }
         if (wave == 0) {                  // the tile's 64 lse and delta values
             const int64_t r0 = ((int64_t)b * p.Hq + h) * Nq;
