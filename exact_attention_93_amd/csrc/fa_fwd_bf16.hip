@@ -96,6 +96,30 @@ __device__ __forceinline__ f32x16_t mfma_bf16(u32x4_t a, u32x4_t b, f32x16_t c)
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// At d = 256 a wavefront owns the whole register file, and the compiler
+// would then put every product in the AGPR form and copy each score tile out
+// for the softmax.  These products are inline assembly with fixed register
+// files instead: S^T and the K, V^T and P^T operands in VGPRs, Q^T and the
+// O^T accumulator in AGPRs.  The compiler does not see their latency, so the
+// gaps the hardware needs between a product and a vector instruction are
+// explicit s_nop statements tied to the registers concerned (d = 256 only):
+// a VALU write of P^T or Q^T read by a product needs 2 wait states (s_nop 3),
+// a product's S^T read by the VALU 11 (s_nop 15), and O^T is read or
+// rewritten by the VALU only after 32.  Accumulating into exactly the
+// previous product's destination needs no gap.
+__device__ __forceinline__ void mma_s_first_v(f32x16_t &d, u32x4_t a, u32x4_t bq)
+{
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(bq));
+}
+__device__ __forceinline__ void mma_s_v(f32x16_t &d, u32x4_t a, u32x4_t bq)
+{
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "a"(bq));
+}
+__device__ __forceinline__ void mma_o_a(f32x16_t &acc, u32x4_t a, u32x4_t b)
+{
+    asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
 // Two floats -> two bf16 (round to nearest even) packed low/high.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
 {
@@ -281,6 +305,16 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
 #pragma unroll
             for (int e = 0; e < 4; ++e) qreg[t][e] = (qreg[t][e] ^ flip) & keep;
     }
+    if constexpr (D == 256) {
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+            const u32x4_t v = qreg[t];
+            asm("; q^T to agpr" : "=a"(qreg[t]) : "0"(v));
+        }
+        asm volatile("s_nop 3" : "+a"(qreg[0]));
+#pragma unroll
+        for (int t = 1; t < KSTEPS; ++t) asm volatile("" : "+a"(qreg[t]));
+    }
 
     // Tile j holds a key this wavefront can see (causal: keys <= its last
     // row + off).  A wavefront whose rows all lie past the end sees nothing.
@@ -327,14 +361,32 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     for (int xb = 0; xb < XB; ++xb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[xb][i] = 0.f;
+    if constexpr (D == 256) {
+#pragma unroll
+        for (int xb = 0; xb < XB; ++xb) {
+            const f32x16_t z = oacc[xb];
+            asm("; o^T to agpr" : "=a"(oacc[xb]) : "0"(z));
+        }
+    }
     f32x16_t sacc[NKB];        // S^T of the tile whose softmax is next
     u32x4_t pb[PVSTEPS];       // P^T (bf16) of the tile whose product is next
+    // d = 256: 32 wait states between the last product into O^T and any
+    // vector access to it.
+    auto sync_acc = [&]() __attribute__((always_inline)) {
+        if constexpr (D == 256) {
+            asm volatile("s_nop 15\n\ts_nop 15" : "+a"(oacc[0]));
+#pragma unroll
+            for (int xb = 1; xb < XB; ++xb) asm volatile("" : "+a"(oacc[xb]));
+        }
+    };
 
     // Matrix-core step for tile j: O^T += V_{j-1}^T P_{j-1}^T, then
     // S_j^T = K_j Q^T.  No vector-ALU work beyond operand addressing.
     auto mfma_step = [&](int j, const uint16_t *kcur, const uint16_t *vprev) {
         if (j >= 1 && visible(j - 1)) {
             const char *vs = (const char *)vprev;
+            if constexpr (D == 256)   // P^T was written by the vector ALU
+                asm volatile("s_nop 3" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]));
 #pragma unroll
             for (int u = 0; u < PVSTEPS; ++u)
 #pragma unroll
@@ -349,7 +401,8 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
                         a[2 * r] = t2[0];
                         a[2 * r + 1] = t2[1];
                     }
-                    oacc[xb] = mfma_bf16(a, pb[u], oacc[xb]);
+                    if constexpr (D == 256) mma_o_a(oacc[xb], a, pb[u]);
+                    else oacc[xb] = mfma_bf16(a, pb[u], oacc[xb]);
                 }
             // Operand reads run PF_PV products ahead of the matrix cores.
 #pragma unroll
@@ -366,15 +419,22 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
             const char *ks = (const char *)kcur;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
+                if constexpr (D != 256) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+                    for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
+                }
                 const int row = kb * 32 + krow;
                 const char *kr = ks + row * ROW_BYTES;
                 const int sw = k_swz<D>(row);
 #pragma unroll
                 for (int t = 0; t < KSTEPS; ++t) {
                     const u32x4_t a = *(const u32x4_t *)(kr + (((2 * t + hf) ^ sw) * 16));
-                    sacc[kb] = mfma_bf16(a, qreg[t], sacc[kb]);
+                    if constexpr (D == 256) {
+                        if (t == 0) mma_s_first_v(sacc[kb], a, qreg[t]);
+                        else mma_s_v(sacc[kb], a, qreg[t]);
+                    } else {
+                        sacc[kb] = mfma_bf16(a, qreg[t], sacc[kb]);
+                    }
                 }
             }
 #pragma unroll
@@ -407,10 +467,13 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
             m_run = m_tile;
         }
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            sync_acc();
 #pragma unroll
-            for (int xb = 0; xb < XB; ++xb)
+            for (int xb = 0; xb < XB; ++xb) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) oacc[xb][i] *= alpha;
+                if constexpr (D == 256) asm volatile("s_nop 3" : "+a"(oacc[xb]));
+            }
         }
         return alpha;
     };
@@ -456,6 +519,9 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     bool ref_set = false;      // block-sparse: the wavefront has set its reference (uniform)
     auto softmax_step = [&](int j) {
         if (!visible(j)) return;
+        if constexpr (D == 256) {   // S^T was written by the products
+            asm volatile("s_nop 15" : "+v"(sacc[0]), "+v"(sacc[1]));
+        }
         const int key0 = key_lo + tix(j) * kBN;
         const bool need_mask = (key0 + kBN > Nk) || (CAUSAL && key0 + kBN - 1 > wq0 + off);
         if (need_mask) {
@@ -539,6 +605,7 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
         }
     }
 
+    sync_acc();
     // ---- epilogue: O = O_acc / l (bf16, round to nearest even), lse = m ln2 + ln l.
     // A row that saw no key (l = 0) gets O = 0 and lse = -inf.  A split
     // forward stores O in fp32 and the log-sum-exp of its key range instead.
