@@ -164,13 +164,14 @@ template <int D> __device__ __forceinline__ int v_swz(int row)
     return D != 64 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
-// 16 bytes per lane from base + off (bytes) straight into LDS at dst + 16*lane,
-// through a buffer descriptor whose range check returns zeros at or past
-// `range` bytes.
-__device__ __forceinline__ void load_lds16(const void *base, int range, uint32_t off, lds_void_t *dst)
+// 16 bytes per lane from base + soff + voff (bytes) straight into LDS at
+// dst + 16*lane, through a buffer descriptor whose range check returns zeros
+// at or past `range` bytes.
+// soff is the wavefront-uniform part of the offset.
+__device__ __forceinline__ void load_lds16(const void *base, int range, uint32_t voff, uint32_t soff, lds_void_t *dst)
 {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, range, 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, soff, 0, 0);
 }
 
 __device__ __forceinline__ void lds_wait_vm()
@@ -325,24 +326,29 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
 
     // ---- HBM -> LDS: each wavefront moves BLKS_PER_WAVE 1 KB blocks of a
     // tile; lane l fills physical chunk l % CHUNKS of row l / CHUNKS.
+    // The per-lane byte offsets within a tile are fixed; the tile's own
+    // offset goes in as the scalar offset, and the LDS destinations are
+    // wavefront-uniform.
     const int ld_row = lane / CHUNKS, ld_pch = lane % CHUNKS;
-    auto load_k = [&](int j, uint16_t *dst) {
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    uint32_t k_voff[BLKS_PER_WAVE], v_voff[BLKS_PER_WAVE];
 #pragma unroll
-        for (int i = 0; i < BLKS_PER_WAVE; ++i) {
-            const int blk = wave * BLKS_PER_WAVE + i;
-            const int row = blk * ROWS_PER_BLK + ld_row;
-            const uint32_t rowoff = (uint32_t)(tix(j) * kBN + row) * (uint32_t)(sK * 2);
-            load_lds16(kbase, range, rowoff + ((ld_pch ^ k_swz<D>(row)) * 16), (lds_void_t *)&dst[blk * 512]);
-        }
+    for (int i = 0; i < BLKS_PER_WAVE; ++i) {
+        const int row = (wave * BLKS_PER_WAVE + i) * ROWS_PER_BLK + ld_row;
+        k_voff[i] = (uint32_t)row * (uint32_t)(sK * 2) + ((ld_pch ^ k_swz<D>(row)) * 16);
+        v_voff[i] = (uint32_t)row * (uint32_t)(sK * 2) + ((ld_pch ^ v_swz<D>(row)) * 16);
+    }
+    auto load_k = [&](int j, uint16_t *dst) {
+        const uint32_t soff = (uint32_t)(tix(j) * kBN) * (uint32_t)(sK * 2);
+#pragma unroll
+        for (int i = 0; i < BLKS_PER_WAVE; ++i)
+            load_lds16(kbase, range, k_voff[i], soff, (lds_void_t *)&dst[(wave_u * BLKS_PER_WAVE + i) * 512]);
     };
     auto load_v = [&](int j, uint16_t *dst) {
+        const uint32_t soff = (uint32_t)(tix(j) * kBN) * (uint32_t)(sK * 2);
 #pragma unroll
-        for (int i = 0; i < BLKS_PER_WAVE; ++i) {
-            const int blk = wave * BLKS_PER_WAVE + i;
-            const int row = blk * ROWS_PER_BLK + ld_row;
-            const uint32_t rowoff = (uint32_t)(tix(j) * kBN + row) * (uint32_t)(sK * 2);
-            load_lds16(vbase, range, rowoff + ((ld_pch ^ v_swz<D>(row)) * 16), (lds_void_t *)&dst[blk * 512]);
-        }
+        for (int i = 0; i < BLKS_PER_WAVE; ++i)
+            load_lds16(vbase, range, v_voff[i], soff, (lds_void_t *)&dst[(wave_u * BLKS_PER_WAVE + i) * 512]);
     };
 
     // A-operand row for lane lq: key 32*kb + perm(lq), perm swaps bits 2 and 3.
