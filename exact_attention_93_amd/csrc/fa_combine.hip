@@ -57,34 +57,36 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(FwdParams p, int spl)
     __shared__ float red_w[kThreads / 16];
     __shared__ __attribute__((aligned(16))) f32x4_t red_o[kThreads];
 
-    // this group's ranges, four at a time: the loads of a batch are issued
-    // together (a range index past the end is clamped and weighted 0), then
-    // merged against the running maximum m without branches.  An empty range
-    // (L_r = -inf) gets weight 0, and while every range so far was empty
-    // (m = -inf) nothing is rescaled.
+    // this group's ranges, four at a time while four remain (the loads of a
+    // batch are issued together), then one at a time; each is merged against
+    // the running maximum m without branches.  An empty range (L_r = -inf)
+    // gets weight 0, and while every range so far was empty (m = -inf)
+    // nothing is rescaled.
     float m = -INFINITY, wsum = 0.f;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    auto merge = [&](float l, f32x4_t o) {
+        const float m_new = fmaxf(m, l);
+        const float a = m_new == -INFINITY ? 1.f : expf(m - m_new);   // 0 when m is -inf
+        const float w = l == -INFINITY ? 0.f : expf(l - m_new);
+        acc = acc * a + w * o;
+        wsum = wsum * a + w;
+        m = m_new;
+    };
     if (live) {
-        for (int r0 = sl; r0 < p.nsplit; r0 += 4 * spl) {
+        int r = sl;
+        for (; r + 3 * spl < p.nsplit; r += 4 * spl) {
             float lr[4];
             f32x4_t o[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int r = min(r0 + k * spl, p.nsplit - 1);
-                lr[k] = p.lse_part[r * rows + row];
-                o[k] = *(const f32x4_t *)(p.o_part + (r * rows + row) * D + x);
+                lr[k] = p.lse_part[(r + k * spl) * rows + row];
+                o[k] = *(const f32x4_t *)(p.o_part + ((r + k * spl) * rows + row) * D + x);
             }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float l = r0 + k * spl < p.nsplit ? lr[k] : -INFINITY;
-                const float m_new = fmaxf(m, l);
-                const float a = m_new == -INFINITY ? 1.f : expf(m - m_new);   // 0 when m is -inf
-                const float w = l == -INFINITY ? 0.f : expf(l - m_new);
-                acc = acc * a + w * o[k];
-                wsum = wsum * a + w;
-                m = m_new;
-            }
+            for (int k = 0; k < 4; ++k) merge(lr[k], o[k]);
         }
+        for (; r < p.nsplit; r += spl)
+            merge(p.lse_part[r * rows + row], *(const f32x4_t *)(p.o_part + (r * rows + row) * D + x));
     }
     red_o[tid] = acc;
     if (chunk == 0) {
