@@ -20,10 +20,11 @@
 // The eight wavefronts form two groups of four, one wavefront of each group
 // per SIMD, that run the same tile sequence one phase apart: while one
 // group issues the matrix-core products of its tile, the other runs the
-// softmax of its previous tile on the vector ALU, and they swap at every
-// barrier.  This is the overlap of softmax with matrix products that the
+// softmax of its previous tile on the vector ALU, and they swap roles
+// halfway through each tile.  This is the overlap of softmax with matrix products that the
 // second page (section 10) describes for FlashAttention-3 ("ping-pong"),
-// built from CDNA barriers instead of Hopper warp specialisation.
+// built from one CDNA workgroup barrier per tile instead of Hopper warp
+// specialisation.
 //
 // Data movement: K and V tiles go from HBM straight into LDS with 16-byte
 // buffer loads (buffer_load_dwordx4 ... lds), double-buffered so that the
@@ -177,15 +178,6 @@ __device__ __forceinline__ void load_lds16(const void *base, int range, uint32_t
 __device__ __forceinline__ void lds_wait_vm()
 {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-// Workgroup barrier that leaves this wavefront's global-to-LDS loads in
-// flight (__syncthreads() would wait for them): only its LDS accesses
-// complete first.  One asm statement with a memory clobber, so no LDS access
-// moves across it.
-__device__ __forceinline__ void barrier_keep_loads()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Block-sparse forward: query blocks of kMaskRows rows x key tiles of kBN
@@ -565,13 +557,17 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
         lb_run = lb_run * alpha + (rs0 + rs1);
     };
 
-    // ---- ping-pong schedule.  Global phase t = 0 .. 2n+1, one barrier
-    // after each.  A wavefront of group g runs local step s = t - g: even
-    // s = 2j is the matrix-core step for tile j, odd s = 2j+1 the vector-ALU
-    // step for tile j.  Group 1 trails group 0 by one phase, so on every SIMD
-    // one wavefront issues matrix-core work while the other runs the softmax.
-    // K_j and V_{j-1} are read in phases 2j and 2j+1; K_{j+1} and V_j are
-    // loaded during those two phases into the other stage.
+    // ---- ping-pong schedule.  Global phase t = 0 .. 2n+1.  A wavefront of
+    // group g runs local step s = t - g: even s = 2j is the matrix-core step
+    // for tile j, odd s = 2j+1 the vector-ALU step for tile j.  Group 1
+    // trails group 0 by one phase, so on every SIMD one wavefront issues
+    // matrix-core work while the other runs the softmax.  K_j and V_{j-1} are
+    // read in phases 2j and 2j+1; K_{j+1} and V_j are loaded during those two
+    // phases into the other stage.  The only barrier is the one after each odd
+    // phase, which the stage swap needs.  Within a tile each wavefront moves
+    // from its first step to its second as soon as it is done: the two
+    // wavefronts of a SIMD still alternate, and neither waits for the slower
+    // wavefronts of the other SIMDs halfway through the tile.
     if (n > 0) load_k(0, Ks0);
     lds_wait_vm();
     __syncthreads();
@@ -596,8 +592,6 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
         if (t & 1) {                         // K_{j+1}, V_j resident before phase 2j+2
             lds_wait_vm();
             __syncthreads();
-        } else {                             // they may still be arriving
-            barrier_keep_loads();
         }
     };
     for (int t = 0; t < nphase; t += 4) {
