@@ -175,6 +175,20 @@ __device__ __forceinline__ void load_lds16(const void *base, int range, uint32_t
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voff, soff, 0, 0);
 }
 
+// The same load as inline assembly, through a descriptor held in SGPRs
+// (base, stride 0, `range` bytes, the same flags), to LDS byte address lds.
+// The compiler does not see it write LDS and adds no waits for it: the
+// caller orders it against the LDS reads with its own vmcnt waits and
+// barriers.  M0 carries the LDS address and needs one wait state before
+// the load.  M0 is a reserved register (a clobber entry would be ignored):
+// the compiler sets it right before each instruction of its own that reads
+// it, and a kernel that uses this load issues no such instruction.
+__device__ __forceinline__ void load_lds16_asm(u32x4_t rsrc, uint32_t voff, uint32_t soff, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds));
+}
+
 __device__ __forceinline__ void lds_wait_vm()
 {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -199,18 +213,25 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     constexpr int ROWS_PER_BLK = 1024 / ROW_BYTES; // rows per 1 KB direct-load block
     constexpr int BLKS = kBN * ROW_BYTES / 1024;   // 1 KB blocks per tile and tensor
     constexpr int NWAVES = kThreads / 64;
-    constexpr int BLKS_PER_WAVE = BLKS / NWAVES;
     constexpr int TILE_ELEMS = kBN * D;
-    static_assert(BLKS_PER_WAVE >= 1 && BLKS % NWAVES == 0, "tile shape");
+    // Tile streams: one per workgroup, or, with a block mask and two
+    // ping-pong groups, one per group.  Each group then owns one query block
+    // of the mask and visits only the tiles that block keeps, with its own
+    // K/V stages, loaded by its own four wavefronts.
+    constexpr int NG = (SPARSE && NWAVES == 8) ? 2 : 1;
+    constexpr int LOADERS = NWAVES / NG;           // wavefronts that load one stream
+    constexpr int BLKS_PER_WAVE = BLKS / LOADERS;
+    static_assert(BLKS_PER_WAVE >= 1 && BLKS % LOADERS == 0, "tile shape");
+    static_assert(!SPARSE || wg_rows<D>() / kMaskRows == NG, "one query block of the mask per stream");
 
     // Two stages of K and V as four distinct objects.  Every access below
     // names its stage statically, so the compiler can see that the loads
     // filling one stage never alias the operand reads of the other and does
     // not make those reads wait for the loads in flight.
-    __shared__ __attribute__((aligned(1024))) uint16_t Ks0[TILE_ELEMS];
-    __shared__ __attribute__((aligned(1024))) uint16_t Ks1[TILE_ELEMS];
-    __shared__ __attribute__((aligned(1024))) uint16_t Vs0[TILE_ELEMS];
-    __shared__ __attribute__((aligned(1024))) uint16_t Vs1[TILE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks0[NG * TILE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t Ks1[NG * TILE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs0[NG * TILE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t Vs1[NG * TILE_ELEMS];
 
     int b, h, tile, split;
     decode_tile(p, b, h, tile, split);
@@ -231,47 +252,6 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     int n = max(0, kt_hi - kt_lo);
     const int key_lo = kt_lo * kBN;
 
-    // ---- block-sparse: the tiles any query block of this workgroup keeps,
-    // in order, each with one bit per query block (bit 14 + block)
-    __shared__ uint16_t tile_list[SPARSE ? kMaxMaskTiles : 1];
-    __shared__ int tile_count;
-    if constexpr (SPARSE) {
-        constexpr int QB = kBM / kMaskRows;         // query blocks per workgroup (2, or 1 at d = 256)
-        if (wave == 0) {
-            const int qb0 = q_first / kMaskRows;
-            const int nqb = p.mask_nqb;
-            const uint8_t *mrow = p.block_mask + ((int64_t)h * nqb + qb0) * p.mask_nkb;
-            int cnt = 0;
-            for (int base = kt_lo; base < kt_hi; base += 64) {
-                const int j = base + lane;
-                int bits = 0;
-                if (j < kt_hi) {
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-                        if (qb0 + qb < nqb && mrow[qb * p.mask_nkb + j]) bits |= 1 << qb;
-                }
-                const uint64_t keep = __builtin_amdgcn_ballot_w64(bits != 0);
-                const int pos = cnt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(keep >> 32),
-                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)keep, 0));
-                if (bits) tile_list[pos] = (uint16_t)(j | (bits << 14));
-                cnt += __builtin_popcountll(keep);
-            }
-            if (lane == 0) tile_count = cnt;
-        }
-        __syncthreads();
-        n = tile_count;
-    }
-    // absolute key-tile index of the loop's j-th tile, and whether this
-    // wavefront's query block keeps it
-    auto tix = [&](int j) -> int {
-        if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane(tile_list[j]) & 0x3fff;
-        else return j;
-    };
-    auto block_keeps = [&](int j) -> bool {
-        if constexpr (SPARSE) return (__builtin_amdgcn_readfirstlane(tile_list[j]) >> (14 + wave * 32 / kMaskRows)) & 1;
-        else return true;
-    };
-
     const int sQ = p.Hq * D, sK = p.Hkv * D;      // row strides (elements)
     const uint16_t *qbase = (const uint16_t *)p.q + ((int64_t)b * Nq * p.Hq + h) * D;
     const uint16_t *kbase = (const uint16_t *)p.k + ((int64_t)b * Nk * p.Hkv + hk) * D + (int64_t)key_lo * sK;
@@ -290,58 +270,132 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
 #pragma unroll
         for (int t = 0; t < KSTEPS; ++t) qreg[t] = u32x4_t{0, 0, 0, 0};
     }
-    if (p.qmode != 0) {
-        const uint32_t keep = p.qmode == 2 ? 0u : 0xffffffffu;
-        const uint32_t flip = p.qmode == 1 ? 0x80008000u : 0u;
+    // The sign or zero fix for the scale, and at d = 256 the move of Q^T to
+    // AGPRs, run just before the tile loop (finish_q), so that nothing waits
+    // for these loads before the first tile's loads are issued.
+    auto finish_q = [&]() {
+        if (p.qmode != 0) {
+            const uint32_t keep = p.qmode == 2 ? 0u : 0xffffffffu;
+            const uint32_t flip = p.qmode == 1 ? 0x80008000u : 0u;
 #pragma unroll
-        for (int t = 0; t < KSTEPS; ++t)
+            for (int t = 0; t < KSTEPS; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) qreg[t][e] = (qreg[t][e] ^ flip) & keep;
-    }
-    if constexpr (D == 256) {
-#pragma unroll
-        for (int t = 0; t < KSTEPS; ++t) {
-            const u32x4_t v = qreg[t];
-            asm("; q^T to agpr" : "=a"(qreg[t]) : "0"(v));
+                for (int e = 0; e < 4; ++e) qreg[t][e] = (qreg[t][e] ^ flip) & keep;
         }
-        asm volatile("s_nop 3" : "+a"(qreg[0]));
+        if constexpr (D == 256) {
 #pragma unroll
-        for (int t = 1; t < KSTEPS; ++t) asm volatile("" : "+a"(qreg[t]));
+            for (int t = 0; t < KSTEPS; ++t) {
+                const u32x4_t v = qreg[t];
+                asm("; q^T to agpr" : "=a"(qreg[t]) : "0"(v));
+            }
+            asm volatile("s_nop 3" : "+a"(qreg[0]));
+#pragma unroll
+            for (int t = 1; t < KSTEPS; ++t) asm volatile("" : "+a"(qreg[t]));
+        }
+    };
+
+    // ---- block-sparse: for each stream (query block of the mask), the key
+    // tiles it keeps, in order.  n becomes this wavefront's own count, and
+    // n_loop the longest stream's, which sets the workgroup's phase count.
+    // Built after the Q^T loads are issued, so that their latency and the
+    // mask reads' overlap; the mask bytes of both streams and four 64-tile
+    // chunks are read together before any of them is compacted.
+    const int sg = NG == 2 ? grp : 0;             // this wavefront's stream
+    __shared__ uint16_t tile_list[SPARSE ? NG : 1][SPARSE ? kMaxMaskTiles : 1];
+    __shared__ int tile_count[NG];
+    int n_loop = n;
+    if constexpr (SPARSE) {
+        if (wave == 0) {
+            constexpr int CB = 4;                 // 64-tile chunks per batch
+            const int qb0 = q_first / kMaskRows;
+            const int nqb = p.mask_nqb;
+            const uint8_t *mrow = p.block_mask + ((int64_t)h * nqb + qb0) * p.mask_nkb;
+            int cnt[NG];
+#pragma unroll
+            for (int qb = 0; qb < NG; ++qb) cnt[qb] = 0;
+            for (int base = kt_lo; base < kt_hi; base += 64 * CB) {
+                bool kept[NG][CB];
+                // every byte is read at a clamped, valid position first (no
+                // branch between the loads), and the bounds applied after
+#pragma unroll
+                for (int qb = 0; qb < NG; ++qb)
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) {
+                        const int j = base + 64 * cb + lane;
+                        const int qr = min(qb, nqb - 1 - qb0), jc = min(j, kt_hi - 1);
+                        const uint8_t m = mrow[qr * p.mask_nkb + jc];
+                        kept[qb][cb] = j < kt_hi && qb0 + qb < nqb && m != 0;
+                    }
+#pragma unroll
+                for (int qb = 0; qb < NG; ++qb)
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) {
+                        const uint64_t keep = __builtin_amdgcn_ballot_w64(kept[qb][cb]);
+                        const int pos = cnt[qb] + (int)__builtin_amdgcn_mbcnt_hi(
+                                            (uint32_t)(keep >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)keep, 0));
+                        if (kept[qb][cb]) tile_list[qb][pos] = (uint16_t)(base + 64 * cb + lane);
+                        cnt[qb] += __builtin_popcountll(keep);
+                    }
+            }
+            if (lane == 0) {
+#pragma unroll
+                for (int qb = 0; qb < NG; ++qb) tile_count[qb] = cnt[qb];
+            }
+        }
+        __syncthreads();
+        n = tile_count[sg];
+        n_loop = NG == 2 ? max(tile_count[0], tile_count[1]) : n;
     }
+    // absolute key-tile index of the j-th tile of this wavefront's stream
+    auto tix = [&](int j) -> int {
+        if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)tile_list[sg][j]);
+        else return j;
+    };
 
     // Tile j holds a key this wavefront can see (causal: keys <= its last
     // row + off).  A wavefront whose rows all lie past the end sees nothing.
     const bool wave_live = wq0 < Nq;
     auto visible = [&](int j) {
-        return wave_live && (!CAUSAL || key_lo + tix(j) * kBN <= wq0 + 31 + off) && block_keeps(j);
+        return wave_live && (!CAUSAL || key_lo + tix(j) * kBN <= wq0 + 31 + off);
     };
 
     // ---- HBM -> LDS: each wavefront moves BLKS_PER_WAVE 1 KB blocks of a
-    // tile; lane l fills physical chunk l % CHUNKS of row l / CHUNKS.
-    // The per-lane byte offsets within a tile are fixed; the tile's own
-    // offset goes in as the scalar offset, and the LDS destinations are
-    // wavefront-uniform.
+    // tile of its stream; lane l fills physical chunk l % CHUNKS of row
+    // l / CHUNKS.  The per-lane byte offsets within a tile are fixed; the
+    // tile's own offset goes in as the scalar offset, and the LDS
+    // destinations are wavefront-uniform.  A stream's tiles sit at element
+    // offset sg * TILE_ELEMS of each stage.
     const int ld_row = lane / CHUNKS, ld_pch = lane % CHUNKS;
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const int wl = NG == 2 ? (wave & 3) : wave;   // index among the stream's loaders
+    const int wl_u = __builtin_amdgcn_readfirstlane(wl);
+    const int so = sg * TILE_ELEMS;               // this stream's part of a stage
     uint32_t k_voff[BLKS_PER_WAVE], v_voff[BLKS_PER_WAVE];
 #pragma unroll
     for (int i = 0; i < BLKS_PER_WAVE; ++i) {
-        const int row = (wave * BLKS_PER_WAVE + i) * ROWS_PER_BLK + ld_row;
+        const int row = (wl * BLKS_PER_WAVE + i) * ROWS_PER_BLK + ld_row;
         k_voff[i] = (uint32_t)row * (uint32_t)(sK * 2) + ((ld_pch ^ k_swz<D>(row)) * 16);
         v_voff[i] = (uint32_t)row * (uint32_t)(sK * 2) + ((ld_pch ^ v_swz<D>(row)) * 16);
     }
-    auto load_k = [&](int j, uint16_t *dst) {
+    // With a block mask the loads are inline assembly (load_lds16_asm): the
+    // two streams' pointers differ at run time, and the kernel's own waits
+    // below order every load against the reads of its stage.
+    const uint64_t kaddr = (uint64_t)kbase, vaddr = (uint64_t)vbase;
+    const u32x4_t k_rsrc = {(uint32_t)kaddr, (uint32_t)(kaddr >> 32) & 0xffffu, (uint32_t)range, 0x00020000u};
+    const u32x4_t v_rsrc = {(uint32_t)vaddr, (uint32_t)(vaddr >> 32) & 0xffffu, (uint32_t)range, 0x00020000u};
+    auto load_tile = [&](const uint16_t *src, const u32x4_t &rsrc, const uint32_t *voff, int j, uint16_t *stage) {
         const uint32_t soff = (uint32_t)(tix(j) * kBN) * (uint32_t)(sK * 2);
 #pragma unroll
-        for (int i = 0; i < BLKS_PER_WAVE; ++i)
-            load_lds16(kbase, range, k_voff[i], soff, (lds_void_t *)&dst[(wave_u * BLKS_PER_WAVE + i) * 512]);
+        for (int i = 0; i < BLKS_PER_WAVE; ++i) {
+            uint16_t *dst = &stage[so + (wl_u * BLKS_PER_WAVE + i) * 512];
+            if constexpr (SPARSE)
+                load_lds16_asm(rsrc, voff[i], soff,
+                               __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)dst));
+            else
+                load_lds16(src, range, voff[i], soff, (lds_void_t *)dst);
+        }
     };
-    auto load_v = [&](int j, uint16_t *dst) {
-        const uint32_t soff = (uint32_t)(tix(j) * kBN) * (uint32_t)(sK * 2);
-#pragma unroll
-        for (int i = 0; i < BLKS_PER_WAVE; ++i)
-            load_lds16(vbase, range, v_voff[i], soff, (lds_void_t *)&dst[(wave_u * BLKS_PER_WAVE + i) * 512]);
-    };
+    auto load_k = [&](int j, uint16_t *stage) { load_tile(kbase, k_rsrc, k_voff, j, stage); };
+    auto load_v = [&](int j, uint16_t *stage) { load_tile(vbase, v_rsrc, v_voff, j, stage); };
 
     // A-operand row for lane lq: key 32*kb + perm(lq), perm swaps bits 2 and 3.
     const int krow = (lq & 0x13) | ((lq & 4) << 1) | ((lq & 8) >> 1);
@@ -382,7 +436,7 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     // S_j^T = K_j Q^T.  No vector-ALU work beyond operand addressing.
     auto mfma_step = [&](int j, const uint16_t *kcur, const uint16_t *vprev) {
         if (j >= 1 && visible(j - 1)) {
-            const char *vs = (const char *)vprev;
+            const char *vs = (const char *)(vprev + so);
             if constexpr (D == 256)   // P^T was written by the vector ALU
                 asm volatile("s_nop 3" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]));
 #pragma unroll
@@ -414,7 +468,7 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
             for (int i = 0; i < PF_PV; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
         if (j < n && visible(j)) {
-            const char *ks = (const char *)kcur;
+            const char *ks = (const char *)(kcur + so);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 if constexpr (D != 256) {
@@ -570,8 +624,15 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     // wavefronts of the other SIMDs halfway through the tile.
     if (n > 0) load_k(0, Ks0);
     lds_wait_vm();
+    // The same wait as a builtin, which the compiler's own wait tracking
+    // sees: the Q^T loads are then known to be complete inside the loop.
+    // Otherwise it may put partial vmcnt waits for them before the first
+    // products of a phase, and those would also wait for tile loads it does
+    // not see (the inline-assembly ones).
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0), expcnt and lgkmcnt unconstrained
+    finish_q();
     __syncthreads();
-    const int nphase = 2 * n + 2;
+    const int nphase = 2 * n_loop + 2;    // the same on every wavefront: barriers match
     auto phase = [&](int t, const uint16_t *kcur, const uint16_t *vprev, uint16_t *knext, uint16_t *vnext) {
         if (!(t & 1)) {                      // start loading K_{j+1}, V_j
             const int j = t >> 1;
