@@ -1,0 +1,83 @@
+"""The largest shapes the library accepts, against the fp64 oracle on
+sampled rows.
+
+The entry points reject a tensor whose rows, plus 256 rows of margin, reach
+2^29 elements per batch entry, so every byte offset the kernels form inside
+one batch entry fits in 32 bits.  These cases sit just below that bound, with
+a ragged tail (N is not a multiple of any tile size): a causal prefill at the
+longest sequence for one head at d = 128, the bf16 decoding path (packed
+query heads, 256 key ranges and the merge) at the longest key sequence, and
+the fp32 split path at the longest key sequence for d = 64.
+"""
+import math
+import random
+
+import pytest
+import torch
+
+import exact_attention_93_amd as fa
+from tests.gpu_util import compare, say
+
+pytestmark = pytest.mark.gpu
+
+LIMIT = 1 << 29            # elements per batch entry of one tensor, margin included
+
+
+def longest(heads, d):
+    """Largest length n with (n + 256) * heads * d < 2^29."""
+    return (LIMIT - 1) // (heads * d) - 256
+
+
+def randn(shape, seed, dtype):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g).to(dtype).contiguous()
+
+
+def rows_to_check(B, Hq, N, seed, extra=8):
+    """Both ends, the tail tile and a few seeded rows, per (b, h)."""
+    rng = random.Random(seed)
+    out = []
+    for b in range(B):
+        for h in range(Hq):
+            rows = {0, 1, 63, 64, 255, 256, N - 257, N - 256, N - 65, N - 2, N - 1}
+            rows |= {rng.randrange(N) for _ in range(extra)}
+            out.extend((b, h, i) for i in sorted(r for r in rows if 0 <= r < N))
+    return out
+
+
+def test_longest_prefill_causal_d128():
+    d, H = 128, 1
+    N = longest(H, d)
+    assert (N + 256) * H * d < LIMIT <= (N + 257) * H * d
+    say(f"case limits prefill N={N} d={d}")
+    q, k, v = (randn((1, N, H, d), 900 + i, torch.bfloat16) for i in range(3))
+    o, lse = fa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=True)
+    torch.cuda.synchronize()
+    rows = rows_to_check(1, H, N, seed=901)
+    compare(q, k, v, True, 1 / math.sqrt(d), o.cpu(), lse.cpu(), rows=rows, label=f"prefill N={N}",
+            exact_bounds=True)
+
+
+def test_longest_decode_bf16_d128():
+    d, Hq, Hkv, Nq = 128, 4, 1, 2
+    Nk = longest(Hkv, d)
+    say(f"case limits decode Nk={Nk} d={d}")
+    assert fa.fa_splitkv_num_splits(1, Hq, Hkv, Nq, Nk, d, 0) == 256
+    q = randn((1, Nq, Hq, d), 910, torch.bfloat16)
+    k = randn((1, Nk, Hkv, d), 911, torch.bfloat16)
+    v = randn((1, Nk, Hkv, d), 912, torch.bfloat16)
+    o, lse = fa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=True, num_splits=0)
+    torch.cuda.synchronize()
+    compare(q, k, v, True, 1 / math.sqrt(d), o.cpu(), lse.cpu(), label=f"decode Nk={Nk}", exact_bounds=True)
+
+
+def test_longest_split_fp32_d64():
+    d, Hq, Hkv, Nq = 64, 2, 1, 3
+    Nk = longest(Hkv, d)
+    say(f"case limits fp32 split Nk={Nk} d={d}")
+    q = randn((1, Nq, Hq, d), 920, torch.float32)
+    k = randn((1, Nk, Hkv, d), 921, torch.float32)
+    v = randn((1, Nk, Hkv, d), 922, torch.float32)
+    o, lse = fa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=False, num_splits=0)
+    torch.cuda.synchronize()
+    compare(q, k, v, False, 1 / math.sqrt(d), o.cpu(), lse.cpu(), label=f"fp32 split Nk={Nk}")
