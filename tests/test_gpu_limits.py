@@ -5,9 +5,12 @@ The entry points reject a tensor whose rows, plus 256 rows of margin, reach
 2^29 elements per batch entry, so every byte offset the kernels form inside
 one batch entry fits in 32 bits.  These cases sit just below that bound, with
 a ragged tail (N is not a multiple of any tile size): a causal prefill at the
-longest sequence for one head at d = 128, the bf16 decoding path (packed
-query heads, 256 key ranges and the merge) at the longest key sequence, and
-the fp32 split path at the longest key sequence for d = 64.
+longest sequence for one head at d = 128 and at d = 256, the fp8 forward
+(one byte per element) at its longest sequence, the bf16 decoding path
+(packed query heads, 256 key ranges and the merge) at the longest key
+sequence, and the fp32 split path at the longest key sequence for d = 64.
+The block-sparse forward has its own bound (a mask row holds at most 1024
+key tiles of 64), and runs at exactly that length.
 """
 import math
 import random
@@ -16,6 +19,8 @@ import pytest
 import torch
 
 import exact_attention_93_amd as fa
+from exact_attention_93_amd import workloads as W
+from tests.fp8_util import compare_fp8, fp8_inputs, gpu_fp8
 from tests.gpu_util import compare, say
 
 pytestmark = pytest.mark.gpu
@@ -81,3 +86,39 @@ def test_longest_split_fp32_d64():
     o, lse = fa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=False, num_splits=0)
     torch.cuda.synchronize()
     compare(q, k, v, False, 1 / math.sqrt(d), o.cpu(), lse.cpu(), label=f"fp32 split Nk={Nk}")
+
+
+def test_longest_prefill_causal_d256():
+    d, H = 256, 1
+    N = longest(H, d)
+    say(f"case limits prefill N={N} d={d}")
+    q, k, v = (randn((1, N, H, d), 930 + i, torch.bfloat16) for i in range(3))
+    o, lse = fa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=True)
+    torch.cuda.synchronize()
+    rows = rows_to_check(1, H, N, seed=931, extra=4)
+    compare(q, k, v, True, 1 / math.sqrt(d), o.cpu(), lse.cpu(), rows=rows, label=f"d256 N={N}",
+            exact_bounds=True)
+
+
+def test_longest_fp8_causal():
+    d, H = 128, 1
+    N = longest(H, d)
+    say(f"case limits fp8 N={N}")
+    ins = fp8_inputs(1, N, H, H, d, seed=940)
+    o, lse = gpu_fp8(*ins, True, 1 / math.sqrt(d))
+    rows = rows_to_check(1, H, N, seed=941, extra=4)
+    compare_fp8(*ins, True, 1 / math.sqrt(d), o, lse, rows=rows, label=f"fp8 N={N}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_longest_blocksparse(causal):
+    d, Hq, Hkv, N = 128, 2, 1, 65536
+    say(f"case limits blocksparse N={N} causal={causal}")
+    q, k, v = (randn((1, N, h, d), 950 + i, torch.bfloat16) for i, h in enumerate((Hq, Hkv, Hkv)))
+    mask = W.random_block_mask(Hq, N, 0.3, seed=951)
+    assert mask.shape == (Hq, 512, 1024)
+    o, lse = fa.fwd_blocksparse(q.cuda(), k.cuda(), v.cuda(), mask.cuda(), causal=causal)
+    torch.cuda.synchronize()
+    rows = rows_to_check(1, Hq, N, seed=952, extra=6)
+    compare(q, k, v, causal, 1 / math.sqrt(d), o.cpu(), lse.cpu(), rows=rows, label=f"blocksparse N={N}",
+            block_mask=mask)
