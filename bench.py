@@ -199,7 +199,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+        print("bench.py: the benchmark runs on one GPU only; --gpus must be 1 "
               "(the forward would shard by (batch, head) with no exchange)", file=sys.stderr)
         sys.exit(2)
 
