@@ -7,8 +7,9 @@ A step is one call of fa_fwd (the whole hot path) over the headline workload:
 causal attention, B=2, H=32, N=4096, d=128, bf16 inputs and output, fp32
 accumulation, synthetic inputs already resident in HBM.  W untimed warm-up
 steps, then exactly K steps between a synchronisation on each side, timed
-with events on the stream the kernel runs on (one event before each launch,
-one after the last).  One JSON line is printed.
+with one pair of events on the stream the kernel runs on (one before the
+first step, one after the last; the spread of single steps comes from a
+separate pass afterwards).  One JSON line is printed.
 
 value = conventional FLOPs (4*B*H*N^2*d, halved for causal) / mean step time.
 roofline: achieved = the same FLOPs per launch / mean launch duration, against
@@ -273,20 +274,32 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    # Timed region: K steps between one pair of events on the launch stream
+    # (an event recorded between steps costs the GPU a few microseconds, which
+    # would distort short steps).
     K = args.steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        ev[i].record(stream)
+    e_start.record(stream)
+    for _ in range(K):
         step()
-    ev[K].record(stream)
+    e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(K)]       # ms per launch
-    total_ms = ev[0].elapsed_time(ev[K])
+    total_ms = e_start.elapsed_time(e_end)
     ms_per_step = total_ms / K
-    mean_launch_ms = sum(per) / K
+    mean_launch_ms = ms_per_step
+    # Spread of single steps, from a separate untimed pass with an event
+    # before each step (these spans include the events' own cost).
+    n_spread = min(K, 50)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread + 1)]
+    for i in range(n_spread):
+        ev[i].record(stream)
+        step()
+    ev[n_spread].record(stream)
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(n_spread)]   # ms per step
     outs = (dq, dk, dv) if bwd else (o, lse)
     if not all(torch.isfinite(t.float()).all() for t in outs):
         print("bench.py: non-finite output", file=sys.stderr)
@@ -331,8 +344,10 @@ def main():
         "roofline": {"bound": "hbm" if hbm_bound else "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic},
-        "timing": {"mean_launch_us": round(mean_launch_ms * 1e3, 2), "min_launch_us": round(min(per) * 1e3, 2),
-                   "max_launch_us": round(max(per) * 1e3, 2), "host_wall_s": round(wall, 4),
+        "timing": {"mean_launch_us": round(mean_launch_ms * 1e3, 2),
+                   "min_launch_us": round(min(per) * 1e3, 2), "max_launch_us": round(max(per) * 1e3, 2),
+                   "min_max_from": f"a separate pass of {n_spread} steps with an event before each step",
+                   "host_wall_s": round(wall, 4),
                    "kernel_source_hash": src_hash},
     }
     if w.Nkv != w.N or splits > 1:
