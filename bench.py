@@ -258,17 +258,44 @@ def main():
     if sparse:
         bmask = w.block_mask().to(dev)
 
-    def step():
-        if sparse:
-            fa.fwd_blocksparse(q, k, v, bmask, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
-        elif fp8:
-            fa.fwd_fp8(q, k, v, qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
-        elif bwd:
-            fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=bws,
-                   stream=stream)
+    # One call through the Python binding validates the arguments; the timed
+    # steps then call the C entry point directly with the same, pre-marshalled
+    # arguments (one ctypes call per step), so that the host keeps ahead of
+    # short steps such as the decode step.
+    lib = fa.load_library()
+    sp = stream.cuda_stream
+    ptr = lambda t: t.data_ptr()
+    if sparse:
+        fa.fwd_blocksparse(q, k, v, bmask, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        entry, cargs = lib.fa_fwd_blocksparse, (ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), w.B, w.Hq, w.Hkv, w.N,
+                                                w.d, w.scale, int(w.causal), ptr(bmask), sp)
+    elif fp8:
+        fa.fwd_fp8(q, k, v, qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
+        entry, cargs = lib.fa_fwd_fp8, (ptr(q), ptr(k), ptr(v), ptr(qd), ptr(kd), ptr(vd), ptr(o), ptr(lse),
+                                        w.B, w.Hq, w.Hkv, w.N, w.d, w.scale, int(w.causal), sp)
+    elif bwd:
+        fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale, dq=dq, dk=dk, dv=dv, workspace=bws,
+               stream=stream)
+        entry, cargs = lib.fa_bwd, (ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), ptr(do), ptr(dq), ptr(dk), ptr(dv),
+                                    w.B, w.Hq, w.Hkv, w.N, w.Nkv, w.d, w.scale, int(w.causal), ptr(bws),
+                                    bws.numel(), sp)
+    else:
+        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream,
+               num_splits=w.splits, workspace=ws)
+        f32 = q.dtype == torch.float32
+        if w.Nkv == w.N and w.splits == 1:
+            entry = lib.fa_fwd_f32 if f32 else lib.fa_fwd
+            cargs = (ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), w.B, w.Hq, w.Hkv, w.N, w.d, w.scale,
+                     int(w.causal), sp)
         else:
-            fa.fwd(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream,
-                   num_splits=w.splits, workspace=ws)
+            entry = lib.fa_fwd_splitkv_f32 if f32 else lib.fa_fwd_splitkv
+            cargs = (ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), w.B, w.Hq, w.Hkv, w.N, w.Nkv, w.d, w.scale,
+                     int(w.causal), w.splits, ptr(ws) if ws is not None else 0,
+                     ws.numel() if ws is not None else 0, sp)
+
+    def step():
+        if entry(*cargs) != 0:
+            raise SystemExit(f"bench.py: {entry.__name__} failed")
 
     for _ in range(args.warmup):
         step()
@@ -345,8 +372,10 @@ def main():
                      "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic},
         "timing": {"mean_launch_us": round(mean_launch_ms * 1e3, 2),
-                   "min_launch_us": round(min(per) * 1e3, 2), "max_launch_us": round(max(per) * 1e3, 2),
-                   "min_max_from": f"a separate pass of {n_spread} steps with an event before each step",
+                   "min_step_us_with_events": round(min(per) * 1e3, 2),
+                   "max_step_us_with_events": round(max(per) * 1e3, 2),
+                   "with_events_from": f"a separate pass of {n_spread} steps with an event before each step "
+                                       "(each event adds GPU time, so these can exceed the mean)",
                    "host_wall_s": round(wall, 4),
                    "kernel_source_hash": src_hash},
     }
