@@ -96,6 +96,28 @@ def load_library(path: str = LIB_PATH):
     return lib
 
 
+def _check_buffer(name, t, shape, dtype, device):
+    """A caller-supplied output: on q's GPU, contiguous, of the shape and
+    dtype the kernels write (they write every element of it, so a smaller
+    or strided buffer would be written out of bounds)."""
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a tensor on {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_workspace(name, t, need, device):
+    """A caller-supplied workspace: contiguous bytes on q's GPU, at least `need` of them."""
+    if not t.is_cuda or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor on {device}")
+    if t.numel() * t.element_size() < need:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, {need} needed")
+
+
 def fa_strerror(status: int) -> str:
     return load_library().fa_strerror(int(status)).decode()
 
@@ -159,8 +181,10 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty_like(q)
+    _check_buffer("fwd: out", out, q.shape, q.dtype, q.device)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check_buffer("fwd: lse", lse, (B, Hq, N), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     bf16 = q.dtype == torch.bfloat16
@@ -172,6 +196,8 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse
         need = fa_splitkv_workspace_size(B, Hq, Hkv, N, Nk, d, num_splits)
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if workspace is not None:
+            _check_workspace("fwd: workspace", workspace, need, q.device)
         ws_ptr = workspace.data_ptr() if workspace is not None else 0
         ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
         entry = fa_fwd_splitkv if bf16 else fa_fwd_splitkv_f32
@@ -213,9 +239,13 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _check_buffer("bwd: dq", dq, q.shape, torch.bfloat16, q.device)
+    _check_buffer("bwd: dk", dk, k.shape, torch.bfloat16, q.device)
+    _check_buffer("bwd: dv", dv, v.shape, torch.bfloat16, q.device)
     need = fa_bwd_workspace_size(B, Hq, Nq)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check_workspace("bwd: workspace", workspace, need, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
@@ -258,8 +288,10 @@ def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal: bool = False, scal
         scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((B, N, Hq, d), dtype=torch.bfloat16, device=q.device)
+    _check_buffer("fwd_fp8: out", out, (B, N, Hq, d), torch.bfloat16, q.device)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check_buffer("fwd_fp8: lse", lse, (B, Hq, N), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(),
@@ -298,8 +330,10 @@ def fwd_blocksparse(q, k, v, block_mask, causal: bool = False, scale: float | No
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out = torch.empty_like(q) if out is None else out
+    _check_buffer("fwd_blocksparse: out", out, q.shape, torch.bfloat16, q.device)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check_buffer("fwd_blocksparse: lse", lse, (B, Hq, N), torch.float32, q.device)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
