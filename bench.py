@@ -84,7 +84,8 @@ def traffic_file(w, bwd: bool):
         return os.path.join(PROFILES, "fa_fwd_bf16_causal_B2_H32_N4096_d128_traffic.txt")
     if w.name.startswith("decode_"):
         return os.path.join(PROFILES, f"fa_decode_bf16_{w.name}_traffic.txt")
-    return None
+    kern = {"fp8": "fwd_fp8", "fp32": "fwd_f32"}.get(w.dtype, "fwd_bf16")
+    return os.path.join(PROFILES, f"fa_{kern}_{w.name}_traffic.txt")
 
 
 def read_traffic(path, src_hash):
