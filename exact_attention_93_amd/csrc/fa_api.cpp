@@ -144,8 +144,15 @@ int validate_and_fill(const void *q, const void *k, const void *v, void *o, floa
     return FA_OK;
 }
 
+// HIP keeps the error of the last failing runtime call until it is read, and a
+// successful launch does not reset it.  Cleared right before this library's
+// launches, so that the check after each launch sees only that launch (an
+// earlier failure elsewhere in the process was returned to its own caller).
+void clear_stale_error() { (void)hipGetLastError(); }
+
 int run(const fa::FwdParams &p, int d, bool bf16, hipStream_t stream)
 {
+    clear_stale_error();
     hipError_t e;
     if (!bf16) e = fa::launch_fwd_f32(p, d, stream);
     else if (d <= 128 && !p.block_mask && fa::use_decode(p.Nq, p.group)) e = fa::launch_decode_bf16(p, d, stream);
@@ -245,6 +252,7 @@ int fa_fwd_fp8(const void *q, const void *k, const void *v, const float *q_desca
     p.q_descale = q_descale;
     p.k_descale = k_descale;
     p.v_descale = v_descale;
+    clear_stale_error();
     return fa::launch_fwd_fp8(p, d, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -308,6 +316,7 @@ int fa_bwd(const void *q, const void *k, const void *v, const void *o, const flo
         p.c = 1.f;
     }
     if (!(p.c >= FLT_MIN) || !isfinite(p.c)) return FA_ERR_SCALE;
+    clear_stale_error();
     return fa::launch_bwd_bf16(p, d, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -318,7 +327,7 @@ const char *fa_strerror(int status)
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "B, Hq, Hkv and the sequence lengths must be >= 1 and within the size limits";
     case FA_ERR_HEADS: return "Hq must be a multiple of Hkv";
-    case FA_ERR_HEADDIM: return "unsupported head dimension (bf16 forward: 64, 128, 256; fp32 forward and backward: 64, 128; fp8: 128)";
+    case FA_ERR_HEADDIM: return "unsupported head dimension (bf16 forward: 64, 128, 256; fp32 forward: 64, 128; backward: 64, 128; fp8: 128)";
     case FA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_SCALE: return "scale must be finite (and |scale|*log2(e) representable)";
     case FA_ERR_ALIAS: return "an output or the workspace overlaps an input or another output";

@@ -39,7 +39,10 @@
  * the function returns a nonzero status and enqueues nothing.  On success the
  * work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the
  * function returns FA_OK without waiting.  FA_ERR_LAUNCH reports a failure
- * that the HIP runtime returned for the launch.  Faults during execution
+ * that the HIP runtime returned for the launch.  (HIP's last-error state is
+ * cleared right before the launches, so that an earlier failure of another
+ * HIP call in the thread, already returned to its own caller, is not
+ * reported as this launch's.)  Faults during execution
  * surface at the caller's next synchronisation.  Non-finite input values
  * propagate into the results (no check is made).  No C++ exception crosses
  * this interface.

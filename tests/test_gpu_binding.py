@@ -96,3 +96,28 @@ def test_fp8_and_blocksparse_reject_bad_outputs():
     with pytest.raises(ValueError):
         fa.fwd_blocksparse(q, k, v, mask, lse=lse)
     assert untouched(lse)
+
+
+def _hip_runtime():
+    """The HIP runtime library this process (and libfa.so) uses."""
+    import ctypes
+    path = next(ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln)
+    hip = ctypes.CDLL(path)
+    hip.hipSetDevice.restype = ctypes.c_int
+    hip.hipSetDevice.argtypes = [ctypes.c_int]
+    return hip
+
+
+def test_stale_runtime_error_does_not_fail_a_launch():
+    """An earlier failed HIP call elsewhere in the process (here a rejected
+    device index) leaves HIP's last-error state set; the entry points still
+    report their own launches as successful."""
+    say("case binding stale runtime error")
+    q, k, v = inputs()
+    hip = _hip_runtime()
+    for call in (lambda: fa.fwd(q, k, v, causal=True),
+                 lambda: fa.fwd(q, k, v, num_splits=3),
+                 lambda: fa.bwd(q, k, v, *fa.fwd(q, k, v, causal=True), torch.randn_like(q), causal=True)):
+        assert hip.hipSetDevice(9999) != 0          # rejected by the runtime, nothing else happens
+        call()
+    torch.cuda.synchronize()
