@@ -145,22 +145,33 @@ def cpu_baseline(w, seconds: float, hbm: bool):
     dt = time.perf_counter() - t0
     sample = (f"all {n} query rows of {w.name}" if n == len(rows) else
               f"{n} of the {len(rows)} query rows of {w.name}, evenly strided over (b, h, i)")
-    if hbm:
-        # the sample's share of the algorithmic bytes
-        nbytes = w.io_bytes * n / len(rows)
-        return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-                "sample": sample + f"; fp64 3-pass oracle, {dt:.1f} s wall; bytes counted as the sample's "
-                                   "share of the workload's algorithmic bytes"}
-    if w.mask:   # kept keys of each sampled row (non-causal block masks)
-        m = mk["block_mask"].numpy().astype(np.float64)
-        keys = np.minimum(w.N - 64 * np.arange(m.shape[2]), 64).astype(np.float64)
-        vis = m[pick[:, 1], pick[:, 2] // 128] @ keys
-    else:
-        vis = visible_keys(w, pick[:, 2])
-    flops = float(4.0 * w.d * vis.sum())
+
+    def work(sel):
+        """The sample's work in the metric's unit: bytes (its share of the
+        workload's algorithmic bytes) or FLOPs (4*d per visible key)."""
+        if hbm:
+            return w.io_bytes * len(sel) / len(rows)
+        if w.mask:   # kept keys of each sampled row (non-causal block masks)
+            m = mk["block_mask"].numpy().astype(np.float64)
+            keys = np.minimum(w.N - 64 * np.arange(m.shape[2]), 64).astype(np.float64)
+            vis = m[sel[:, 1], sel[:, 2] // 128] @ keys
+        else:
+            vis = visible_keys(w, sel[:, 2])
+        return float(4.0 * w.d * vis.sum())
+
+    # The same oracle on one thread, over every `threads`-th row of the sample.
+    one = pick[::threads]
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, w.scale, w.causal, rows=one, threads=1, **mk)
+    dt1 = time.perf_counter() - t0
+    scale_unit, unit = (1e9, "GB/s") if hbm else (1e12, "TFLOP/s")
+    what = ("bytes counted as the sample's share of the workload's algorithmic bytes" if hbm
+            else "FLOPs counted as 4*d per visible key")
     return {
-        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-        "sample": sample + f"; fp64 3-pass oracle, {dt:.1f} s wall; FLOPs counted as 4*d per visible key",
+        "value": work(pick) / dt / scale_unit, "unit": unit, "cores": threads, "kind": "oracle",
+        "sample": sample + f"; fp64 3-pass oracle, {dt:.1f} s wall; {what}",
+        "single_thread": {"value": work(one) / dt1 / scale_unit, "unit": unit, "cores": 1,
+                          "sample": f"{len(one)} of those rows (every {threads}th), {dt1:.1f} s wall"},
     }
 
 
