@@ -121,6 +121,14 @@ __device__ __forceinline__ void mma_o_a(f32x16_t &acc, u32x4_t a, u32x4_t b)
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// 16x16x32 product (D = A*B + C); lane l holds row/column l % 16 of A/B and
+// the K slots of group l / 16, and rows 4*(l/16) .. +3 of column l % 16 of D.
+__device__ __forceinline__ f32x4_t mfma16_bf16(u32x4_t a, u32x4_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 // Two floats -> two bf16 (round to nearest even) packed low/high.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
 {
@@ -420,6 +428,21 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
             asm("; o^T to agpr" : "=a"(oacc[xb]) : "0"(z));
         }
     }
+    // d <= 128: the sum of the bf16 probabilities is taken on the matrix
+    // cores, with one 16x16x32 product per 16 keys whose B operand is the same
+    // P^T register quad the O^T products read.  (A v_dot2 on the vector ALU
+    // waits for the matrix pipeline whenever the other wavefront of the SIMD
+    // is issuing products, which is all of the softmax phase.)  Read as a
+    // 16x32 B operand, lane l's quad holds keys of half (l / 32) for query
+    // l % 32, i.e. query n + 16 (g % 2) for column n = l % 16 and K group
+    // g = l / 16.  The 0/1 A operand selects, for output rows 4r .. 4r+3, the
+    // K groups with g % 2 == r % 2, so every accumulator register of lane l
+    // ends up holding the 16-key sum of its own query l % 32, both halves
+    // included.  The accumulator is rescaled together with O^T.
+    constexpr bool MSUM = D != 256;
+    f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t sel_w = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? 0x3f803f80u : 0u;
+    const u32x4_t sum_sel = {sel_w, sel_w, sel_w, sel_w};
     f32x16_t sacc[NKB];        // S^T of the tile whose softmax is next
     u32x4_t pb[PVSTEPS];       // P^T (bf16) of the tile whose product is next
     // d = 256: 32 wait states between the last product into O^T and any
@@ -439,6 +462,10 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
             const char *vs = (const char *)(vprev + so);
             if constexpr (D == 256)   // P^T was written by the vector ALU
                 asm volatile("s_nop 3" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]));
+            if constexpr (MSUM) {
+#pragma unroll
+                for (int u = 0; u < PVSTEPS; ++u) lacc = mfma16_bf16(sum_sel, pb[u], lacc);
+            }
 #pragma unroll
             for (int u = 0; u < PVSTEPS; ++u)
 #pragma unroll
@@ -456,9 +483,12 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
                     if constexpr (D == 256) mma_o_a(oacc[xb], a, pb[u]);
                     else oacc[xb] = mfma_bf16(a, pb[u], oacc[xb]);
                 }
-            // Operand reads run PF_PV products ahead of the matrix cores.
+            // Operand reads run PF_PV products ahead of the matrix cores; the
+            // row-sum products, whose operands are already in registers, go
+            // first while those reads are in flight.
 #pragma unroll
             for (int i = 0; i < PF_PV; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            if constexpr (MSUM) __builtin_amdgcn_sched_group_barrier(0x008, PVSTEPS, 0);
 #pragma unroll
             for (int i = 0; i < PVSTEPS * XB - PF_PV; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -501,13 +531,6 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
         }
     };
 
-    // Vector-ALU step for tile j: mask (tiles crossing the diagonal or the
-    // end only), tile maximum, reference-maximum update with the rare
-    // accumulator rescale, P = 2^(s*c - m) rounded to bf16 and packed as the
-    // next product's B operand, and both row sums: fp32 over the unrounded
-    // values (the log-sum-exp), and over the bf16 values the product consumes
-    // (two per v_dot2_f32_bf16 against (1, 1)), which normalises O so that O
-    // stays a convex combination of the V rows.
     // Reference-maximum update for a tile whose raw row maximum is mx, with
     // the accumulator rescale; returns the factor for the running sums.
     auto settle = [&](float mx) -> float {
@@ -525,6 +548,10 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
 #pragma unroll
                 for (int i = 0; i < 16; ++i) oacc[xb][i] *= alpha;
                 if constexpr (D == 256) asm volatile("s_nop 3" : "+a"(oacc[xb]));
+            }
+            if constexpr (MSUM) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lacc[i] *= alpha;
             }
         }
         return alpha;
@@ -560,9 +587,9 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     // Vector-ALU step for tile j: mask (tiles crossing the diagonal or the
     // end only), the probabilities against the reference maximum, and both
     // row sums: fp32 over the unrounded values (the log-sum-exp), and over the
-    // bf16 values the product consumes (two per v_dot2_f32_bf16 against
-    // (1, 1)), which normalises O so that O stays a convex combination of the
-    // V rows.  The reference maximum is set from the exact maximum of the
+    // bf16 values the product consumes, which normalises O so that O stays a
+    // convex combination of the V rows (on the matrix cores for d <= 128, see
+    // lacc; at d = 256 two per v_dot2_f32_bf16 against (1, 1)).  The reference maximum is set from the exact maximum of the
     // first tile only; later tiles are exponentiated against it directly,
     // since any reference gives the same softmax (second page, section 5.1).
     // Should a row's scores run more than 64 (base 2) above the reference,
@@ -599,16 +626,18 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
             alpha *= settle(tile_max());
             rf = exps();
         }
-        float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-        for (int u = 0; u < PVSTEPS; ++u) {
-            rs0 = sum_bf16x2(pb[u][0], rs0);
-            rs1 = sum_bf16x2(pb[u][1], rs1);
-            rs0 = sum_bf16x2(pb[u][2], rs0);
-            rs1 = sum_bf16x2(pb[u][3], rs1);
-        }
         l_run = l_run * alpha + rf;
-        lb_run = lb_run * alpha + (rs0 + rs1);
+        if constexpr (!MSUM) {
+            float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+            for (int u = 0; u < PVSTEPS; ++u) {
+                rs0 = sum_bf16x2(pb[u][0], rs0);
+                rs1 = sum_bf16x2(pb[u][1], rs1);
+                rs0 = sum_bf16x2(pb[u][2], rs0);
+                rs1 = sum_bf16x2(pb[u][3], rs1);
+            }
+            lb_run = lb_run * alpha + (rs0 + rs1);
+        }
     };
 
     // ---- ping-pong schedule.  Global phase t = 0 .. 2n+1.  A wavefront of
@@ -671,7 +700,7 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     // A row that saw no key (l = 0) gets O = 0 and lse = -inf.  A split
     // forward stores O in fp32 and the log-sum-exp of its key range instead.
     const float l_tot = sum_halves(l_run);
-    const float lb_tot = sum_halves(lb_run);
+    const float lb_tot = MSUM ? lacc[0] : sum_halves(lb_run);
     if (my_q < Nq) {
         const bool empty = l_tot == 0.f;
         const float inv = empty ? 0.f : 1.f / lb_tot;
