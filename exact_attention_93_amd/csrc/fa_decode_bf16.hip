@@ -60,16 +60,18 @@ __device__ __forceinline__ f32x16_t mfma_bf16(u32x4_t a, u32x4_t b, f32x16_t c)
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// 16x16x32 product (D = A*B + C); lane l holds row/column l % 16 of A/B and
+// the K slots of group l / 16, and rows 4*(l/16) .. +3 of column l % 16 of D.
+__device__ __forceinline__ f32x4_t mfma16_bf16(u32x4_t a, u32x4_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
 {
     f32x2_t f = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
-}
-
-__device__ __forceinline__ float sum_bf16x2(uint32_t pair, float acc)
-{
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pair),
-                                           __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
 }
 
 // Combine a value of this lane with the one of lane ^ 32 (v_permlane32_swap).
@@ -205,8 +207,18 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(FwdParams p)
         for (int t = 0; t < KSTEPS; ++t) kr[t] = src[2 * t + hf];
     };
 
-    float m_run = -INFINITY, l_run = 0.f, lb_run = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
     f32x16_t oacc[XB];
+    // The sum of the bf16 probabilities is taken on the matrix cores: one
+    // 16x16x32 product per 16 keys with the P^T quad as B operand and a 0/1
+    // selector as A, so that every accumulator register of lane l holds the
+    // sum for its own query row l % 32 over both lane halves (rows 4r .. 4r+3
+    // of the output take the K groups g = l / 16 with g % 2 == r % 2).  A
+    // v_dot2 on the vector ALU would wait for the matrix pipeline while
+    // another wavefront of the SIMD issues products.
+    f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};
+    const uint32_t sel_w = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? 0x3f803f80u : 0u;
+    const u32x4_t sum_sel = {sel_w, sel_w, sel_w, sel_w};
 #pragma unroll
     for (int xb = 0; xb < XB; ++xb)
 #pragma unroll
@@ -233,7 +245,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(FwdParams p)
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_sub);
         m_run = m_new;
         u32x4_t pb[2];
-        float rf = 0.f, rb0 = 0.f;
+        float rf = 0.f;
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -242,10 +254,11 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(FwdParams p)
                 const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * u + 2 * w2 + 1], c, -m_sub));
                 rf += e0 + e1;
                 pb[u][w2] = pack_bf16(e0, e1);
-                rb0 = sum_bf16x2(pb[u][w2], rb0);
             }
         l_run = l_run * alpha + rf;
-        lb_run = lb_run * alpha + rb0;
+        lacc *= alpha;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) lacc = mfma16_bf16(sum_sel, pb[u], lacc);
         const char *vs = (const char *)&vst[wave * TILE];
 #pragma unroll
         for (int xb = 0; xb < XB; ++xb) {
@@ -283,7 +296,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_bf16_kernel(FwdParams p)
 
     // ---- merge the four wavefronts (m in base-2 units; O unnormalised)
     const float l_tot = sum_halves(l_run);
-    const float lb_tot = sum_halves(lb_run);
+    const float lb_tot = lacc[0];
     __syncthreads();                                     // every V tile has been read
     if (hf == 0) {
         Mm[wave * kRows + lq] = m_run;
