@@ -87,7 +87,11 @@ template <int D> constexpr int wg_threads() { return 64 * wg_waves<D>(); }
 template <int D> constexpr int wg_rows() { return 32 * wg_waves<D>(); }   // query rows per workgroup
 constexpr float kLazyLog2 = 8.0f;
 constexpr float kFarSum = 0x1p64f;   // tile row sum that signals a stale reference maximum
-constexpr int PF_PV = 4;       // products whose V^T operands are read ahead of the matrix cores
+// Products whose V^T operands are read ahead of the matrix cores (measured:
+// at d = 128 the four row-sum products that open the phase cover most of the
+// LDS latency, so two suffice; d = 64 has half the products per phase and
+// gains from six).  d = 256 keeps four.
+template <int D> constexpr int pf_pv() { return D == 64 ? 6 : D == 128 ? 2 : 4; }
 constexpr int PF_QK = 4;       // products whose K operands are read ahead of the matrix cores
 constexpr float kLn2 = 0.693147180559945309f;
 
@@ -483,19 +487,19 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
                     if constexpr (D == 256) mma_o_a(oacc[xb], a, pb[u]);
                     else oacc[xb] = mfma_bf16(a, pb[u], oacc[xb]);
                 }
-            // Operand reads run PF_PV products ahead of the matrix cores; the
+            // Operand reads run pf_pv<D>() products ahead of the matrix cores; the
             // row-sum products, whose operands are already in registers, go
             // first while those reads are in flight.
 #pragma unroll
-            for (int i = 0; i < PF_PV; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            for (int i = 0; i < pf_pv<D>(); ++i) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             if constexpr (MSUM) __builtin_amdgcn_sched_group_barrier(0x008, PVSTEPS, 0);
 #pragma unroll
-            for (int i = 0; i < PVSTEPS * XB - PF_PV; ++i) {
+            for (int i = 0; i < PVSTEPS * XB - pf_pv<D>(); ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
 #pragma unroll
-            for (int i = 0; i < PF_PV; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            for (int i = 0; i < pf_pv<D>(); ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
         if (j < n && visible(j)) {
             const char *ks = (const char *)(kcur + so);
