@@ -92,7 +92,9 @@ constexpr float kFarSum = 0x1p64f;   // tile row sum that signals a stale refere
 // LDS latency, so two suffice; d = 64 has half the products per phase and
 // gains from six).  d = 256 keeps four.
 template <int D> constexpr int pf_pv() { return D == 64 ? 6 : D == 128 ? 2 : 4; }
-constexpr int PF_QK = 4;       // products whose K operands are read ahead of the matrix cores
+// Products whose K operands are read ahead of the matrix cores (measured: two
+// at d = 64, four otherwise).
+template <int D> constexpr int pf_qk() { return D == 64 ? 2 : 4; }
 constexpr float kLn2 = 0.693147180559945309f;
 
 __device__ __forceinline__ f32x16_t mfma_bf16(u32x4_t a, u32x4_t b, f32x16_t c)
@@ -524,14 +526,14 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
                 }
             }
 #pragma unroll
-            for (int i = 0; i < PF_QK; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int i = 0; i < pf_qk<D>(); ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
-            for (int i = 0; i < NKB * KSTEPS - PF_QK; ++i) {
+            for (int i = 0; i < NKB * KSTEPS - pf_qk<D>(); ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
 #pragma unroll
-            for (int i = 0; i < PF_QK; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            for (int i = 0; i < pf_qk<D>(); ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
     };
 
