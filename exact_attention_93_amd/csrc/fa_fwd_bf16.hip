@@ -77,6 +77,9 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
+// A compile-time integer passed as an argument to a generic lambda.
+template <int V> struct ic { static constexpr int value = V; };
+
 constexpr int kBN = 64;        // keys per K/V tile
 // Wavefronts per workgroup: 8 (two per SIMD, the two groups of the
 // ping-pong), or 4 at d = 256, where one wavefront's Q and O^T alone take
@@ -287,7 +290,7 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     // The sign or zero fix for the scale, and at d = 256 the move of Q^T to
     // AGPRs, run just before the tile loop (finish_q), so that nothing waits
     // for these loads before the first tile's loads are issued.
-    auto finish_q = [&]() {
+    auto finish_q = [&]() __attribute__((always_inline)) {
         if (p.qmode != 0) {
             const uint32_t keep = p.qmode == 2 ? 0u : 0xffffffffu;
             const uint32_t flip = p.qmode == 1 ? 0x80008000u : 0u;
@@ -361,7 +364,7 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
         n_loop = NG == 2 ? max(tile_count[0], tile_count[1]) : n;
     }
     // absolute key-tile index of the j-th tile of this wavefront's stream
-    auto tix = [&](int j) -> int {
+    auto tix = [&](int j) __attribute__((always_inline)) -> int {
         if constexpr (SPARSE) return __builtin_amdgcn_readfirstlane((int)tile_list[sg][j]);
         else return j;
     };
@@ -369,7 +372,7 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     // Tile j holds a key this wavefront can see (causal: keys <= its last
     // row + off).  A wavefront whose rows all lie past the end sees nothing.
     const bool wave_live = wq0 < Nq;
-    auto visible = [&](int j) {
+    auto visible = [&](int j) __attribute__((always_inline)) {
         return wave_live && (!CAUSAL || key_lo + tix(j) * kBN <= wq0 + 31 + off);
     };
 
@@ -396,7 +399,7 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     const uint64_t kaddr = (uint64_t)kbase, vaddr = (uint64_t)vbase;
     const u32x4_t k_rsrc = {(uint32_t)kaddr, (uint32_t)(kaddr >> 32) & 0xffffu, (uint32_t)range, 0x00020000u};
     const u32x4_t v_rsrc = {(uint32_t)vaddr, (uint32_t)(vaddr >> 32) & 0xffffu, (uint32_t)range, 0x00020000u};
-    auto load_tile = [&](const uint16_t *src, const u32x4_t &rsrc, const uint32_t *voff, int j, uint16_t *stage) {
+    auto load_tile = [&](const uint16_t *src, const u32x4_t &rsrc, const uint32_t *voff, int j, uint16_t *stage) __attribute__((always_inline)) {
         const uint32_t soff = (uint32_t)(tix(j) * kBN) * (uint32_t)(sK * 2);
 #pragma unroll
         for (int i = 0; i < BLKS_PER_WAVE; ++i) {
@@ -408,8 +411,45 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
                 load_lds16(src, range, voff[i], soff, (lds_void_t *)dst);
         }
     };
-    auto load_k = [&](int j, uint16_t *stage) { load_tile(kbase, k_rsrc, k_voff, j, stage); };
-    auto load_v = [&](int j, uint16_t *stage) { load_tile(vbase, v_rsrc, v_voff, j, stage); };
+    auto load_k = [&](int j, uint16_t *stage) __attribute__((always_inline)) { load_tile(kbase, k_rsrc, k_voff, j, stage); };
+    auto load_v = [&](int j, uint16_t *stage) __attribute__((always_inline)) { load_tile(vbase, v_rsrc, v_voff, j, stage); };
+    // Dense streams (no block mask): the loads of even phase 2*jl, K_{jl+1}
+    // and V_{jl}, are issued by the wavefronts whose matrix-core step runs in
+    // that phase (the leading group; at d = 256 all four), spread among their
+    // products: V blocks among the P V products, K blocks among the score
+    // products.  (Issued by all eight wavefronts back to back at the start of
+    // the phase, they kept each one waiting ~350 cycles per tile on the
+    // vector-memory path.)  The loads are straight-line code with no branch,
+    // so that they share a scheduling region with the products; a tile that
+    // does not exist is "loaded" through a zero-length range, which moves no
+    // data.
+    constexpr bool SPREAD = !SPARSE;
+    constexpr int SPREAD_LOADERS = NWAVES == 8 ? 4 : NWAVES;
+    constexpr int BPL = BLKS / SPREAD_LOADERS;    // blocks per loader and tensor
+    const int wl4 = __builtin_amdgcn_readfirstlane(wave & (SPREAD_LOADERS - 1));
+    uint32_t k_voff4[SPREAD ? BPL : 1], v_voff4[SPREAD ? BPL : 1];
+    if constexpr (SPREAD) {
+#pragma unroll
+        for (int i = 0; i < BPL; ++i) {
+            const int row = (wl4 * BPL + i) * ROWS_PER_BLK + ld_row;
+            k_voff4[i] = (uint32_t)row * (uint32_t)(sK * 2) + ((ld_pch ^ k_swz<D>(row)) * 16);
+            v_voff4[i] = (uint32_t)row * (uint32_t)(sK * 2) + ((ld_pch ^ v_swz<D>(row)) * 16);
+        }
+    }
+    auto issue_k = [&](int jl, uint16_t *knext) __attribute__((always_inline)) {
+        const int krange = jl + 1 < n ? range : 0;
+        const uint32_t soff = (uint32_t)((jl + 1) * kBN) * (uint32_t)(sK * 2);
+#pragma unroll
+        for (int i = 0; i < BPL; ++i)
+            load_lds16(kbase, krange, k_voff4[i], soff, (lds_void_t *)&knext[(wl4 * BPL + i) * 512]);
+    };
+    auto issue_v = [&](int jl, uint16_t *vnext) __attribute__((always_inline)) {
+        const int vrange = jl < n ? range : 0;
+        const uint32_t soff = (uint32_t)(jl * kBN) * (uint32_t)(sK * 2);
+#pragma unroll
+        for (int i = 0; i < BPL; ++i)
+            load_lds16(vbase, vrange, v_voff4[i], soff, (lds_void_t *)&vnext[(wl4 * BPL + i) * 512]);
+    };
 
     // A-operand row for lane lq: key 32*kb + perm(lq), perm swaps bits 2 and 3.
     const int krow = (lq & 0x13) | ((lq & 4) << 1) | ((lq & 8) >> 1);
@@ -463,7 +503,12 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
 
     // Matrix-core step for tile j: O^T += V_{j-1}^T P_{j-1}^T, then
     // S_j^T = K_j Q^T.  No vector-ALU work beyond operand addressing.
-    auto mfma_step = [&](int j, const uint16_t *kcur, const uint16_t *vprev) {
+    // With LOADS (a compile-time ic<0 or 1>), the tile loads of the phase
+    // (K_{jl+1}, V_{jl}) are spread among the products: V blocks among the
+    // P V products, K blocks among the score products.
+    auto mfma_step = [&](auto LOADS, int j, const uint16_t *kcur, const uint16_t *vprev, int jl,
+                         uint16_t *knext, uint16_t *vnext) __attribute__((always_inline)) {
+        constexpr bool LD = decltype(LOADS)::value != 0;
         if (j >= 1 && visible(j - 1)) {
             const char *vs = (const char *)(vprev + so);
             if constexpr (D == 256)   // P^T was written by the vector ALU
@@ -492,11 +537,12 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
             // Operand reads run pf_pv<D>() products ahead of the matrix cores; the
             // row-sum products, whose operands are already in registers, go
             // first while those reads are in flight.
+            constexpr int NP = PVSTEPS * XB;
 #pragma unroll
             for (int i = 0; i < pf_pv<D>(); ++i) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             if constexpr (MSUM) __builtin_amdgcn_sched_group_barrier(0x008, PVSTEPS, 0);
 #pragma unroll
-            for (int i = 0; i < PVSTEPS * XB - pf_pv<D>(); ++i) {
+            for (int i = 0; i < NP - pf_pv<D>(); ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
@@ -504,6 +550,7 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
             for (int i = 0; i < pf_pv<D>(); ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
         if (j < n && visible(j)) {
+            if constexpr (LD) { issue_v(jl, vnext); issue_k(jl, knext); }
             const char *ks = (const char *)(kcur + so);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
@@ -525,21 +572,29 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
                     }
                 }
             }
+            // the phase's 2*BPL loads go evenly after the product / operand-read pairs
+            constexpr int NS = NKB * KSTEPS, NIT = NS - pf_qk<D>(), NL = 2 * BPL;
 #pragma unroll
             for (int i = 0; i < pf_qk<D>(); ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
-            for (int i = 0; i < NKB * KSTEPS - pf_qk<D>(); ++i) {
+            for (int i = 0; i < NIT; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+                for (int r = 0; r < NL; ++r)
+                    if (LD && r * NIT / NL == i) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
             }
 #pragma unroll
             for (int i = 0; i < pf_qk<D>(); ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        } else if constexpr (LD) {
+            issue_v(jl, vnext);
+            issue_k(jl, knext);
         }
     };
 
     // Reference-maximum update for a tile whose raw row maximum is mx, with
     // the accumulator rescale; returns the factor for the running sums.
-    auto settle = [&](float mx) -> float {
+    auto settle = [&](float mx) __attribute__((always_inline)) -> float {
         const float m_tile = mx * c;
         const bool grow = m_tile > m_run + kLazyLog2;
         float alpha = 1.f;
@@ -562,7 +617,7 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
         }
         return alpha;
     };
-    auto tile_max = [&]() {
+    auto tile_max = [&]() __attribute__((always_inline)) {
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -572,7 +627,7 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     };
     // P = 2^(s*c - m) rounded to bf16 and packed as the next product's B
     // operand; returns the fp32 row sum of the unrounded values.
-    auto exps = [&]() -> float {
+    auto exps = [&]() __attribute__((always_inline)) -> float {
         const float m_sub = m_run == -INFINITY ? 0.f : m_run;
         float rf0 = 0.f, rf1 = 0.f;
 #pragma unroll
@@ -602,7 +657,7 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     // its tile sum exceeds 2^64 (or overflows), and that tile is redone with
     // its own maximum and the usual rescale.
     bool ref_set = false;      // block-sparse: the wavefront has set its reference (uniform)
-    auto softmax_step = [&](int j) {
+    auto softmax_step = [&](int j) __attribute__((always_inline)) {
         if (!visible(j)) return;
         if constexpr (D == 256) {   // S^T was written by the products
             asm volatile("s_nop 15" : "+v"(sacc[0]), "+v"(sacc[1]));
@@ -668,37 +723,58 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     finish_q();
     __syncthreads();
     const int nphase = 2 * n_loop + 2;    // the same on every wavefront: barriers match
-    auto phase = [&](int t, const uint16_t *kcur, const uint16_t *vprev, uint16_t *knext, uint16_t *vnext) {
-        if (!(t & 1)) {                      // start loading K_{j+1}, V_j
+    // G: the wavefront's group; P: the parity of global phase t (both
+    // compile-time, so that each group's loop is straight-line code with its
+    // loads in the same scheduling regions as its products).
+    auto phase = [&](auto G, auto P, int t, const uint16_t *kcur, const uint16_t *vprev, uint16_t *knext,
+                     uint16_t *vnext) __attribute__((always_inline)) {
+        constexpr int g = decltype(G)::value, par = decltype(P)::value;
+        // Even phases load K_{j+1} and V_j (j = t/2): with a block mask at the
+        // start of the phase, otherwise spread through the leading group's
+        // products.
+        if constexpr (!SPREAD && par == 0) {
             const int j = t >> 1;
             if (j + 1 < n) load_k(j + 1, knext);
             if (j < n) load_v(j, vnext);
         }
-        const int s = t - grp;
+        constexpr bool LD = SPREAD && par == 0 && g == 0;
+        constexpr bool MSTEP = ((par - g) & 1) == 0;   // local step s = t - g is even
+        const int s = t - g;
         if (s >= 0 && s <= 2 * n) {
-            if (!(s & 1)) {
+            if constexpr (MSTEP) {
                 // Matrix-core phases issue first when both wavefronts of a SIMD are ready.
                 __builtin_amdgcn_s_setprio(1);
-                mfma_step(s >> 1, kcur, vprev);
+                mfma_step(ic<LD>(), s >> 1, kcur, vprev, t >> 1, knext, vnext);
                 __builtin_amdgcn_s_setprio(0);
             } else {
                 softmax_step(s >> 1);
             }
+        } else if constexpr (LD) {
+            issue_v(t >> 1, vnext);
+            issue_k(t >> 1, knext);
         }
-        if (t & 1) {                         // K_{j+1}, V_j resident before phase 2j+2
+        if constexpr (par == 1) {            // K_{j+1}, V_j resident before phase 2j+2
             lds_wait_vm();
             __syncthreads();
         }
     };
-    for (int t = 0; t < nphase; t += 4) {
-        // even j = t/2: K_j in Ks0, V_{j-1} in Vs1; loads go to Ks1, Vs0
-        phase(t, Ks0, Vs1, Ks1, Vs0);
-        phase(t + 1, Ks0, Vs1, Ks1, Vs0);
-        if (t + 2 < nphase) {
-            // odd j: K_j in Ks1, V_{j-1} in Vs0; loads go to Ks0, Vs1
-            phase(t + 2, Ks1, Vs0, Ks0, Vs1);
-            phase(t + 3, Ks1, Vs0, Ks0, Vs1);
+    auto run = [&](auto G) __attribute__((always_inline)) {
+        for (int t = 0; t < nphase; t += 4) {
+            // even j = t/2: K_j in Ks0, V_{j-1} in Vs1; loads go to Ks1, Vs0
+            phase(G, ic<0>(), t, Ks0, Vs1, Ks1, Vs0);
+            phase(G, ic<1>(), t + 1, Ks0, Vs1, Ks1, Vs0);
+            if (t + 2 < nphase) {
+                // odd j: K_j in Ks1, V_{j-1} in Vs0; loads go to Ks0, Vs1
+                phase(G, ic<0>(), t + 2, Ks1, Vs0, Ks0, Vs1);
+                phase(G, ic<1>(), t + 3, Ks1, Vs0, Ks0, Vs1);
+            }
         }
+    };
+    if constexpr (NWAVES == 8) {
+        if (grp == 0) run(ic<0>());
+        else run(ic<1>());
+    } else {
+        run(ic<0>());
     }
 
     sync_acc();
