@@ -29,7 +29,8 @@ import os
 
 from ._build import LIB_PATH
 
-__all__ = ["fwd", "fwd_blocksparse", "fa_fwd_blocksparse", "fwd_fp8", "fa_fwd_fp8", "bwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_splitkv_num_splits",
+__all__ = ["fwd", "fwd_blocksparse", "fa_fwd_blocksparse", "fwd_fp8", "fa_fwd_fp8", "fwd_fp8_block",
+           "fa_fwd_fp8_block", "quantize_fp8", "fa_quantize_fp8", "bwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_splitkv_num_splits",
            "fa_splitkv_workspace_size", "fa_strerror", "fa_version", "load_library", "FAError",
            "STATUS", "EXPORTS"]
 
@@ -39,8 +40,8 @@ STATUS = {
     "FA_ERR_SPLITS": 9, "FA_ERR_WORKSPACE": 10,
 }
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_splitkv_num_splits",
-           "fa_splitkv_workspace_size", "fa_fwd_blocksparse", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_size", "fa_strerror",
-           "fa_version")
+           "fa_splitkv_workspace_size", "fa_fwd_blocksparse", "fa_fwd_fp8", "fa_fwd_fp8_block", "fa_quantize_fp8",
+           "fa_bwd", "fa_bwd_workspace_size", "fa_strerror", "fa_version")
 
 _lib = None
 
@@ -82,6 +83,11 @@ def load_library(path: str = LIB_PATH):
     lib.fa_fwd_fp8.restype = ctypes.c_int
     lib.fa_fwd_fp8.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
                                ctypes.c_void_p])
+    lib.fa_fwd_fp8_block.restype = ctypes.c_int
+    lib.fa_fwd_fp8_block.argtypes = ([ctypes.c_void_p] * 8 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
+                                     ctypes.c_void_p])
+    lib.fa_quantize_fp8.restype = ctypes.c_int
+    lib.fa_quantize_fp8.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4 + [ctypes.c_void_p] * 2
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd.argtypes = ([ctypes.c_void_p] * 9 + [ctypes.c_int] * 6 + [ctypes.c_float, ctypes.c_int,
                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p])
@@ -297,6 +303,92 @@ def fwd_fp8(q, k, v, q_descale, k_descale, v_descale, causal: bool = False, scal
     st = fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_descale.data_ptr(), k_descale.data_ptr(),
                     v_descale.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d, scale, causal,
                     stream.cuda_stream)
+    if st != 0:
+        raise FAError(st, fa_strerror(st))
+    return out, lse
+
+
+QUANT_BLOCK = 64         # rows per block of the block-scaled fp8 format
+
+
+def fa_quantize_fp8(x, codes, exps, B, N, H, d, signs, stream) -> int:
+    return load_library().fa_quantize_fp8(x, codes, exps, B, N, H, d, signs, stream)
+
+
+def quantize_fp8(x, signs=None, codes=None, exps=None, stream=None):
+    """Block-scaled e4m3 quantisation through libfa.so.  Returns (codes, exps).
+
+    x: bf16 GPU tensor [B, N, H, 128].  signs: None, or an int8 GPU tensor of
+    128 values +-1, which rotates every row first, y = (x * signs) H (H the
+    Sylvester-Hadamard matrix; rotating both q and k multiplies the scores by
+    128, see fwd_fp8_block).  codes: uint8 [B, N, H, 128] (e4m3 codes);
+    exps: int8 [B, H, ceil(N / 64)]; the real block values are code * 2^exp."""
+    import torch
+
+    if not x.is_cuda or x.dtype != torch.bfloat16 or x.dim() != 4 or not x.is_contiguous():
+        raise ValueError("quantize_fp8: x must be a contiguous bfloat16 GPU tensor [B, N, H, d]")
+    B, N, H, d = x.shape
+    nb = -(-N // QUANT_BLOCK)
+    if signs is not None:
+        if not signs.is_cuda or signs.dtype != torch.int8 or tuple(signs.shape) != (d,) or not signs.is_contiguous():
+            raise ValueError(f"quantize_fp8: signs must be a contiguous int8 GPU tensor of {d} values")
+    codes = torch.empty((B, N, H, d), dtype=torch.uint8, device=x.device) if codes is None else codes
+    exps = torch.empty((B, H, nb), dtype=torch.int8, device=x.device) if exps is None else exps
+    _check_buffer("quantize_fp8: codes", codes, (B, N, H, d), torch.uint8, x.device)
+    _check_buffer("quantize_fp8: exps", exps, (B, H, nb), torch.int8, x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device)
+    st = fa_quantize_fp8(x.data_ptr(), codes.data_ptr(), exps.data_ptr(), B, N, H, d,
+                         signs.data_ptr() if signs is not None else 0, stream.cuda_stream)
+    if st != 0:
+        raise FAError(st, fa_strerror(st))
+    return codes, exps
+
+
+def fa_fwd_fp8_block(q, k, v, qe, ke, ve, o, lse, B, Hq, Hkv, N, d, scale, causal, stream) -> int:
+    return load_library().fa_fwd_fp8_block(q, k, v, qe, ke, ve, o, lse, B, Hq, Hkv, N, d, float(scale),
+                                           int(causal), stream)
+
+
+def fwd_fp8_block(q, k, v, q_exp, k_exp, v_exp, causal: bool = False, scale: float | None = None, out=None,
+                  lse=None, stream=None):
+    """fp8 attention forward with per-block scales through libfa.so.
+    Returns (o bf16, lse).
+
+    q: [B, N, Hq, 128], k, v: [B, N, Hkv, 128] e4m3 codes (uint8 or
+    torch.float8_e4m3fn); q_exp [B, Hq, ceil(N/64)], k_exp and v_exp
+    [B, Hkv, ceil(N/64)] int8: the real inputs are code * 2^exp of their
+    64-row block (quantize_fp8's output).  When q and k were both rotated by
+    quantize_fp8 with the same signs, pass scale / 128 (the rotation
+    multiplies every score by 128)."""
+    import torch
+
+    ts = (q, k, v, q_exp, k_exp, v_exp)
+    if not all(t.is_cuda for t in ts):
+        raise ValueError("fwd_fp8_block: every tensor must be on the GPU (there is no CPU path)")
+    if any(t.element_size() != 1 for t in ts):
+        raise ValueError("fwd_fp8_block: codes and exponents are one byte each")
+    if not all(t.is_contiguous() for t in ts):
+        raise ValueError("fwd_fp8_block: tensors must be contiguous")
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    nb = -(-N // QUANT_BLOCK)
+    if (tuple(k.shape) != (B, N, Hkv, d) or v.shape != k.shape or tuple(q_exp.shape) != (B, Hq, nb)
+            or tuple(k_exp.shape) != (B, Hkv, nb) or tuple(v_exp.shape) != (B, Hkv, nb)):
+        raise ValueError("fwd_fp8_block: shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, N, Hq, d), dtype=torch.bfloat16, device=q.device)
+    _check_buffer("fwd_fp8_block: out", out, (B, N, Hq, d), torch.bfloat16, q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check_buffer("fwd_fp8_block: lse", lse, (B, Hq, N), torch.float32, q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = fa_fwd_fp8_block(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_exp.data_ptr(), k_exp.data_ptr(),
+                          v_exp.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d, scale, causal,
+                          stream.cuda_stream)
     if st != 0:
         raise FAError(st, fa_strerror(st))
     return out, lse

@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 105;  // 0.1.5
+constexpr int kVersion = 200;  // 0.2.0
 constexpr int kMaxSplits = 256;
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb)
@@ -106,6 +106,7 @@ int validate_and_fill(const void *q, const void *k, const void *v, void *o, floa
     p.o_part = nullptr;
     p.lse_part = nullptr;
     p.q_descale = p.k_descale = p.v_descale = nullptr;
+    p.q_exp = p.k_exp = p.v_exp = nullptr;
     p.block_mask = nullptr;
     p.mask_nqb = p.mask_nkb = 0;
     if (nsplit > 1) {
@@ -254,6 +255,54 @@ int fa_fwd_fp8(const void *q, const void *k, const void *v, const float *q_desca
     p.v_descale = v_descale;
     clear_stale_error();
     return fa::launch_fwd_fp8(p, d, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_fwd_fp8_block(const void *q, const void *k, const void *v, const signed char *q_exp,
+                     const signed char *k_exp, const signed char *v_exp, void *o, float *lse, int B, int Hq,
+                     int Hkv, int N, int d, float scale, int causal, void *stream)
+{
+    if (!q_exp || !k_exp || !v_exp) return FA_ERR_NULL;
+    if (d != 128) return (!q || !k || !v || !o || !lse) ? FA_ERR_NULL : FA_ERR_HEADDIM;
+    fa::FwdParams p;
+    const int st = validate_and_fill(q, k, v, o, lse, B, Hq, Hkv, N, N, d, scale, causal, 1,
+                                     nullptr, 0, 1, p, 2);
+    if (st != FA_OK) return st;
+    // the exponent arrays must not overlap the outputs
+    const size_t nb = (size_t)cdiv(N, fa::kQuantBlock);
+    const size_t no = (size_t)B * N * Hq * d * 2, nl = (size_t)B * Hq * N * sizeof(float);
+    const void *ex[3] = {q_exp, k_exp, v_exp};
+    const size_t exn[3] = {(size_t)B * Hq * nb, (size_t)B * Hkv * nb, (size_t)B * Hkv * nb};
+    for (int i = 0; i < 3; ++i)
+        if (overlaps(o, no, ex[i], exn[i]) || overlaps(lse, nl, ex[i], exn[i])) return FA_ERR_ALIAS;
+    p.q_exp = (const int8_t *)q_exp;
+    p.k_exp = (const int8_t *)k_exp;
+    p.v_exp = (const int8_t *)v_exp;
+    clear_stale_error();
+    return fa::launch_fwd_fp8(p, d, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fa_quantize_fp8(const void *x, void *codes, signed char *exps, int B, int N, int H, int d,
+                    const signed char *signs, void *stream)
+{
+    if (!x || !codes || !exps) return FA_ERR_NULL;
+    if (B < 1 || N < 1 || H < 1) return FA_ERR_SHAPE;
+    if (d != 128) return FA_ERR_HEADDIM;
+    if (((int64_t)N + fa::kQuantBlock) * H * d >= ((int64_t)1 << 29)) return FA_ERR_SHAPE;
+    const int64_t nb = cdiv(N, fa::kQuantBlock);
+    if ((int64_t)B * H * nb >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
+    if (((uintptr_t)x & 15) || ((uintptr_t)codes & 7) || ((uintptr_t)signs & 7)) return FA_ERR_ALIGN;
+    const size_t nx = (size_t)B * N * H * d * 2, nc = (size_t)B * N * H * d, ne = (size_t)B * H * nb;
+    if (overlaps(codes, nc, x, nx) || overlaps(exps, ne, x, nx) || overlaps(exps, ne, codes, nc) ||
+        (signs && (overlaps(signs, d, codes, nc) || overlaps(signs, d, exps, ne))))
+        return FA_ERR_ALIAS;
+    fa::QuantParams p;
+    p.x = x;
+    p.codes = codes;
+    p.exps = (int8_t *)exps;
+    p.signs = (const int8_t *)signs;
+    p.B = B; p.N = N; p.H = H;
+    clear_stale_error();
+    return fa::launch_quant_fp8(p, (hipStream_t)stream) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 size_t fa_bwd_workspace_size(int B, int Hq, int Nq)

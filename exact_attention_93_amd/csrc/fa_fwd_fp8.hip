@@ -61,6 +61,14 @@ __device__ __forceinline__ f32x16_t mfma_fp8(i32x8_t a, i32x8_t b, f32x16_t c)
 {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
+// The same product with block scales 2^(sa - 127) on A and 2^(sb - 127) on B
+// (E8M0 codes in the low byte).  Measured lane layout: the scale of operand
+// row (A) or column (B) i over contraction half h comes from lane i + 32 h,
+// the lane that holds that half of the row or column.
+__device__ __forceinline__ f32x16_t mfma_fp8_scaled(i32x8_t a, i32x8_t b, f32x16_t c, int sa, int sb)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
 {
@@ -112,7 +120,9 @@ __device__ __forceinline__ void barrier_keep_loads()
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <bool CAUSAL>
+// BLK: per-block scales (one power of two per 64 rows of Q, K and V, applied
+// by the products themselves) instead of one factor per (batch, head).
+template <bool CAUSAL, bool BLK>
 __global__ void __launch_bounds__(kThreads, 1) fwd_fp8_kernel(FwdParams p)
 {
     constexpr int KSTEPS = D / 64;                 // K-steps of S^T = K Q^T
@@ -140,9 +150,17 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_fp8_kernel(FwdParams p)
     const int q_first = tile * kBM;
     const int wq0 = q_first + wave * 32;
     const int my_q = wq0 + lq;
-    // score scale in base 2 with both dequantisation factors folded in
-    const float c = p.c * p.q_descale[b * p.Hq + h] * p.k_descale[b * p.Hkv + hk];
-    const float vscale = p.v_descale[b * p.Hkv + hk];
+    // score scale in base 2 with both dequantisation factors folded in (per
+    // (batch, head)); with block scales the products apply them instead
+    const float c = BLK ? p.c : p.c * p.q_descale[b * p.Hq + h] * p.k_descale[b * p.Hkv + hk];
+    const float vscale = BLK ? 1.f : p.v_descale[b * p.Hkv + hk];
+    // block scales as E8M0 codes: Q's for this wavefront's 32 rows (they lie
+    // in one 64-row block), K's and V's per 64-key tile (kQuantBlock == kBN)
+    static_assert(kQuantBlock == kBN && kQuantBlock % 32 == 0, "one scale per key tile");
+    const int nbq = (N + kQuantBlock - 1) / kQuantBlock;
+    const int8_t *kexp = BLK ? p.k_exp + (int64_t)(b * p.Hkv + hk) * nbq : nullptr;
+    const int8_t *vexp = BLK ? p.v_exp + (int64_t)(b * p.Hkv + hk) * nbq : nullptr;
+    const int sq = BLK ? 127 + p.q_exp[(int64_t)(b * p.Hq + h) * nbq + min(wq0 / kQuantBlock, nbq - 1)] : 127;
 
     const int sQ = p.Hq * D, sK = p.Hkv * D;
     const uint8_t *qbase = (const uint8_t *)p.q + ((int64_t)b * N * p.Hq + h) * D;
@@ -206,7 +224,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_fp8_kernel(FwdParams p)
     f32x16_t sacc[NKB];
     i32x8_t pb;                // P'^T (e4m3) of the tile whose product is next
 
-    auto mfma_step = [&](int j, const uint8_t *kcur, const uint8_t *vprev) {
+    auto mfma_step = [&](int j, const uint8_t *kcur, const uint8_t *vprev, int sk, int sv) {
         if (j >= 1 && visible(j - 1)) {
             const char *vs = (const char *)vprev;
 #pragma unroll
@@ -220,7 +238,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_fp8_kernel(FwdParams p)
                     a[2 * jb] = t2[0];
                     a[2 * jb + 1] = t2[1];
                 }
-                oacc[xb] = mfma_fp8(a, pb, oacc[xb]);
+                oacc[xb] = BLK ? mfma_fp8_scaled(a, pb, oacc[xb], sv, 127) : mfma_fp8(a, pb, oacc[xb]);
             }
             lacc = mfma_fp8(ones, pb, lacc);
         }
@@ -239,7 +257,7 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_fp8_kernel(FwdParams p)
                     const u32x4_t hi = *(const u32x4_t *)(kr + (((4 * t + 2 * hf + 1) ^ sw) * 16));
                     const i32x8_t a = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-                    sacc[kb] = mfma_fp8(a, qreg[t], sacc[kb]);
+                    sacc[kb] = BLK ? mfma_fp8_scaled(a, qreg[t], sacc[kb], sk, sq) : mfma_fp8(a, qreg[t], sacc[kb]);
                 }
             }
         }
@@ -294,17 +312,28 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_fp8_kernel(FwdParams p)
     lds_wait_vm();
     __syncthreads();
     const int nphase = 2 * n + 2;
-    auto phase = [&](int t, const uint8_t *kcur, const uint8_t *vprev, uint8_t *knext, uint8_t *vnext) {
+    // Block-scale codes of the tiles, loaded with the tiles themselves and
+    // kept per stage like them: sk0/sk1 for K_j (j even/odd), sv0/sv1 for V_j.
+    int sk0 = 127, sk1 = 127, sv0 = 127, sv1 = 127;
+    if (BLK && n > 0) sk0 = 127 + kexp[0];
+    auto phase = [&](int t, const uint8_t *kcur, const uint8_t *vprev, uint8_t *knext, uint8_t *vnext,
+                     const int &skc, const int &svp, int &skn, int &svn) {
         if (!(t & 1)) {
             const int j = t >> 1;
-            if (j + 1 < n) load_k(j + 1, knext);
-            if (j < n) load_v(j, vnext);
+            if (j + 1 < n) {
+                load_k(j + 1, knext);
+                if (BLK) skn = 127 + kexp[j + 1];
+            }
+            if (j < n) {
+                load_v(j, vnext);
+                if (BLK) svn = 127 + vexp[j];
+            }
         }
         const int s = t - grp;
         if (s >= 0 && s <= 2 * n) {
             if (!(s & 1)) {
                 __builtin_amdgcn_s_setprio(1);
-                mfma_step(s >> 1, kcur, vprev);
+                mfma_step(s >> 1, kcur, vprev, skc, svp);
                 __builtin_amdgcn_s_setprio(0);
             } else {
                 softmax_step(s >> 1);
@@ -318,11 +347,11 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_fp8_kernel(FwdParams p)
         }
     };
     for (int t = 0; t < nphase; t += 4) {
-        phase(t, Ks0, Vs1, Ks1, Vs0);
-        phase(t + 1, Ks0, Vs1, Ks1, Vs0);
+        phase(t, Ks0, Vs1, Ks1, Vs0, sk0, sv1, sk1, sv0);
+        phase(t + 1, Ks0, Vs1, Ks1, Vs0, sk0, sv1, sk1, sv0);
         if (t + 2 < nphase) {
-            phase(t + 2, Ks1, Vs0, Ks0, Vs1);
-            phase(t + 3, Ks1, Vs0, Ks0, Vs1);
+            phase(t + 2, Ks1, Vs0, Ks0, Vs1, sk1, sv0, sk0, sv1);
+            phase(t + 3, Ks1, Vs0, Ks0, Vs1, sk1, sv0, sk0, sv1);
         }
     }
 
@@ -346,11 +375,11 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_fp8_kernel(FwdParams p)
     }
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool BLK>
 hipError_t launch_one(const FwdParams &p, hipStream_t stream)
 {
     const unsigned grid = (unsigned)p.B * (unsigned)p.Hq * (unsigned)p.ntiles;
-    hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL, BLK>), dim3(grid), dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -361,7 +390,9 @@ hipError_t launch_fwd_fp8(const FwdParams &p_in, int d, hipStream_t stream)
     if (d != D) return hipErrorInvalidValue;
     FwdParams p = p_in;
     p.ntiles = (p.Nq + kBM - 1) / kBM;
-    return p.causal ? launch_one<true>(p, stream) : launch_one<false>(p, stream);
+    if (p.q_exp)
+        return p.causal ? launch_one<true, true>(p, stream) : launch_one<false, true>(p, stream);
+    return p.causal ? launch_one<true, false>(p, stream) : launch_one<false, false>(p, stream);
 }
 
 }  // namespace fa

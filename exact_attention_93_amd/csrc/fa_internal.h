@@ -32,6 +32,11 @@ struct FwdParams {
     const float *q_descale;   // [B][Hq]
     const float *k_descale;   // [B][Hkv]
     const float *v_descale;   // [B][Hkv]
+    // fp8 forward with per-block scales (NULL: per (batch, head) descales above):
+    // real value = code * 2^exp, one exp per 64 rows of a head
+    const int8_t *q_exp;      // [B][Hq][ceil(Nq / 64)]
+    const int8_t *k_exp;      // [B][Hkv][ceil(Nk / 64)]
+    const int8_t *v_exp;      // [B][Hkv][ceil(Nk / 64)]
     // block-sparse forward: mask [Hq][mask_nqb][mask_nkb] over 128 query rows x 64 keys (NULL: dense)
     const uint8_t *block_mask;
     int mask_nqb, mask_nkb;
@@ -64,6 +69,18 @@ struct BwdParams {
     float scale;                        // the signed scale (dq = scale dS K, dk = scale dS^T Q)
 };
 hipError_t launch_bwd_bf16(const BwdParams &p, int d, hipStream_t stream);
+
+// Block-scaled e4m3 quantisation (fa_quant_fp8.hip): rows per block, and
+// the arguments.
+constexpr int kQuantBlock = 64;
+struct QuantParams {
+    const void *x;          // bf16 [B][N][H][128]
+    void *codes;            // e4m3 [B][N][H][128]
+    int8_t *exps;           // [B][H][ceil(N / 64)]: block value = code * 2^exp
+    const int8_t *signs;    // [128] of +-1 (rotation), or NULL (none)
+    int B, N, H;
+};
+hipError_t launch_quant_fp8(const QuantParams &p, hipStream_t stream);
 
 // Merge of the nsplit partial results into o (bf16 when out_bf16, else fp32) and lse.
 hipError_t launch_combine(const FwdParams &p, int d, int out_bf16, hipStream_t stream);

@@ -212,6 +212,59 @@ def dequantize_fp8(codes: torch.Tensor, descale: torch.Tensor) -> torch.Tensor:
     return (codes.to(torch.float32) * descale[:, None, :, None]).contiguous()
 
 
+QUANT_BLOCK = 64    # rows per block of the block-scaled fp8 format
+
+
+def random_signs(d: int, seed: int) -> torch.Tensor:
+    """d random signs (+1 / -1, int8) for the rotation of the block-scaled fp8
+    path, from a CPU generator seeded with ``seed``."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return (torch.randint(0, 2, (d,), generator=g, dtype=torch.int8) * 2 - 1).contiguous()
+
+
+def random_block_codes(B: int, N: int, H: int, d: int, seed: int, exp_range=(-3, 3)):
+    """Seeded block-scaled fp8 inputs: e4m3 codes of randn values (uint8
+    [B, N, H, d]) and one exponent per 64 rows of a head (int8
+    [B, H, ceil(N / 64)], uniform in exp_range).  The real values are
+    code * 2^exp."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    codes = torch.randn((B, N, H, d), generator=g).to(torch.float8_e4m3fn).view(torch.uint8)
+    nb = (N + QUANT_BLOCK - 1) // QUANT_BLOCK
+    exps = torch.randint(exp_range[0], exp_range[1] + 1, (B, H, nb), generator=g, dtype=torch.int8)
+    return codes.contiguous(), exps.contiguous()
+
+
+def outlier_inputs(B: int, N: int, Hq: int, Hkv: int, d: int, seed: int, channels: int = 2,
+                   channel_gain: float = 30.0, shared_channels: bool = True, rare: float = 0.0,
+                   growth: float = 0.0):
+    """bf16 q, k, v [B, N, H, d]: randn values with the structure that makes
+    low-precision attention hard, each part optional:
+    * outlier channels: ``channels`` of the d coordinates of q and k
+      multiplied by ``channel_gain`` in every row, the same coordinates in q
+      and k when ``shared_channels``, else drawn separately;
+    * rare outliers: each element of q, k and v gains an extra
+      N(0, 10^2) draw with probability ``rare``;
+    * growth along the sequence: 64-row block r of q, k and v multiplied by
+      2^(growth * (r - last block)), so the first blocks are the smallest."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    q = torch.randn((B, N, Hq, d), generator=g)
+    k = torch.randn((B, N, Hkv, d), generator=g)
+    v = torch.randn((B, N, Hkv, d), generator=g)
+    if channels:
+        cq = torch.randperm(d, generator=g)[:channels]
+        ck = cq if shared_channels else torch.randperm(d, generator=g)[:channels]
+        q[..., cq] *= channel_gain
+        k[..., ck] *= channel_gain
+    if rare:
+        q, k, v = (t + (torch.rand(t.shape, generator=g) < rare) * torch.randn(t.shape, generator=g) * 10
+                   for t in (q, k, v))
+    if growth:
+        nb = (N + QUANT_BLOCK - 1) // QUANT_BLOCK
+        f = torch.repeat_interleave(2.0 ** (growth * (torch.arange(nb) - (nb - 1))), QUANT_BLOCK)[:N]
+        q, k, v = (t * f[None, :, None, None] for t in (q, k, v))
+    return tuple(t.to(torch.bfloat16).contiguous() for t in (q, k, v))
+
+
 def sample_rows(w: Workload, per_head: int = 512, seed: int | None = None):
     """Query rows to check, as (b, h, i) triples.
 

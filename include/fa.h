@@ -187,6 +187,52 @@ int fa_fwd_fp8(const void *q, const void *k, const void *v, const float *q_desca
                int B, int Hq, int Hkv, int N, int d, float scale, int causal, void *stream);
 
 /*
+ * fa_fwd_fp8_block -- the fp8 forward with per-block scales: the block
+ * quantisation that the second page ("FlashAttention：IO 感知的精确注意力",
+ * section 10, FlashAttention-3's FP8 path; section 12.2) recommends over one
+ * scale per tensor.  A block is 64 consecutive rows (sequence positions) of
+ * one head, and its scale a power of two:
+ *   q, k, v   : e4m3 codes laid out as fa_fwd_fp8's (one byte each);
+ *   q_exp     : int8 [B][Hq][ceil(N/64)], k_exp and v_exp : int8
+ *               [B][Hkv][ceil(N/64)] (device); the real input of row n of
+ *               head h is code * 2^exp[b][h][n / 64] (fa_quantize_fp8 writes
+ *               such codes and exponents).
+ * The scales are applied exactly by the matrix cores' block-scaled fp8
+ * products.  Output, probabilities, normalisation, error bound and
+ * arguments otherwise as fa_fwd_fp8 (d must be 128; the exponent pointers
+ * must be non-NULL and must not overlap o or lse).
+ */
+int fa_fwd_fp8_block(const void *q, const void *k, const void *v, const signed char *q_exp,
+                     const signed char *k_exp, const signed char *v_exp, void *o, float *lse,
+                     int B, int Hq, int Hkv, int N, int d, float scale, int causal, void *stream);
+
+/*
+ * fa_quantize_fp8 -- block-scaled e4m3 quantisation of a bf16 tensor for
+ * fa_fwd_fp8_block, with optional incoherent processing (the rotation that
+ * spreads outlier coordinates before quantisation, same page, section 10).
+ *   x      : bf16 [B][N][H][d] (device), d = 128;
+ *   signs  : NULL, or int8 [d] of +1 / -1 (device, 8-byte aligned): each row
+ *            is first rotated, y = (x * signs) H, H the d x d
+ *            Sylvester-Hadamard matrix (H[i][j] = (-1)^popcount(i & j)),
+ *            computed in fp32 by the radix-2 butterfly network in stage
+ *            order h = 1, 2, 4, ..., d/2.  Rotating both q and k with the
+ *            same signs multiplies every score by d exactly, so the
+ *            attention takes scale / d; v is not rotated.
+ *   codes  : e4m3 [B][N][H][d] (device, 8-byte aligned), written;
+ *   exps   : int8 [B][H][ceil(N/64)] (device), written: for each block of
+ *            64 rows of a head, the smallest e with max|y| / 2^e <= 448 (the
+ *            largest e4m3 value), -127 for an all-zero block; the codes are
+ *            the e4m3 values nearest to y / 2^e, ties to even.
+ * Rows whose |x| * d overflows fp32 are not supported (no check is made).
+ * Returns FA_ERR_NULL, FA_ERR_SHAPE (sizes as fa_fwd's limits),
+ * FA_ERR_HEADDIM (d != 128), FA_ERR_ALIGN (x 16-byte, codes and signs
+ * 8-byte), FA_ERR_ALIAS (outputs overlapping inputs or each other) before
+ * any HIP call, else FA_OK or FA_ERR_LAUNCH.
+ */
+int fa_quantize_fp8(const void *x, void *codes, signed char *exps, int B, int N, int H, int d,
+                    const signed char *signs, void *stream);
+
+/*
  * fa_bwd -- gradients of the bf16 forward (fa_fwd / fa_fwd_splitkv) for an
  * upstream gradient dout = dL/do.
  *

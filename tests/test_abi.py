@@ -46,7 +46,7 @@ def test_status_codes_match_header():
 
 
 def test_version_and_strerror(lib):
-    assert fa.fa_version() == 105
+    assert fa.fa_version() == 200
     for st in range(11):
         assert fa.fa_strerror(st)
     assert "unknown" in fa.fa_strerror(99)
@@ -224,3 +224,41 @@ def test_invalid_arguments_blocksparse(lib):
     assert mcall(Hq=3) == S["FA_ERR_HEADS"]
     assert mcall(o=O + 2) == S["FA_ERR_ALIGN"]
     assert mcall(lse=Q) == S["FA_ERR_ALIAS"]
+
+
+def test_invalid_arguments_fp8_block(lib):
+    S = fa.STATUS
+    QE, KE, VE = 0xB0000000, 0xB0001000, 0xB0002000
+
+    def fcall(q=Q, k=K, v=V, qe=QE, ke=KE, ve=VE, o=O, lse=L, **kw):
+        a = dict(B=1, Hq=4, Hkv=2, N=16, d=128, scale=0.1, causal=1)
+        a.update(kw)
+        return fa.fa_fwd_fp8_block(q, k, v, qe, ke, ve, o, lse, a["B"], a["Hq"], a["Hkv"], a["N"], a["d"],
+                                   a["scale"], a["causal"], None)
+    assert fcall(ve=None) == S["FA_ERR_NULL"]
+    assert fcall(k=None) == S["FA_ERR_NULL"]
+    assert fcall(d=64) == S["FA_ERR_HEADDIM"]
+    assert fcall(q=Q + 4) == S["FA_ERR_ALIGN"]
+    assert fcall(N=0) == S["FA_ERR_SHAPE"]
+    assert fcall(Hq=3) == S["FA_ERR_HEADS"]
+    assert fcall(scale=float("inf")) == S["FA_ERR_SCALE"]
+    assert fcall(qe=O + 8) == S["FA_ERR_ALIAS"]        # exponents inside the output
+    assert fcall(ke=L) == S["FA_ERR_ALIAS"]            # exponents on lse
+
+
+def test_invalid_arguments_quantize_fp8(lib):
+    S = fa.STATUS
+    X, C, E, SG = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+    def qcall(x=X, c=C, e=E, sg=SG, B=1, N=100, H=2, d=128):
+        return fa.fa_quantize_fp8(x, c, e, B, N, H, d, sg, None)
+    assert qcall(x=None) == S["FA_ERR_NULL"]
+    assert qcall(e=None) == S["FA_ERR_NULL"]
+    assert qcall(N=0) == S["FA_ERR_SHAPE"]
+    assert qcall(N=(1 << 29) // 256) == S["FA_ERR_SHAPE"]
+    assert qcall(d=64) == S["FA_ERR_HEADDIM"]
+    assert qcall(x=X + 8) == S["FA_ERR_ALIGN"]
+    assert qcall(c=C + 4) == S["FA_ERR_ALIGN"]
+    assert qcall(sg=SG + 1) == S["FA_ERR_ALIGN"]
+    assert qcall(c=X + 64) == S["FA_ERR_ALIAS"]       # codes over the input
+    assert qcall(e=C + 16) == S["FA_ERR_ALIAS"]       # exponents over the codes

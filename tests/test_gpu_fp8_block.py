@@ -1,0 +1,178 @@
+"""The block-scaled fp8 path against the oracle (oracle/fp8.py and the fp64
+attention): fa_quantize_fp8 bit for bit (codes and exponents, with and
+without the Hadamard rotation), fa_fwd_fp8_block within the e4m3 bound of
+tests/fp8_util.py, and the error reduction the second page attributes to
+per-block scales and incoherent processing, on inputs with outliers."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_attention_93_amd as fa
+import oracle
+from exact_attention_93_amd import workloads as W
+from oracle import fp8 as F
+from tests.fp8_util import compare_fp8_real, dequantize_blocks_f32
+from tests.gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_quantize(x, signs):
+    codes, exps = fa.quantize_fp8(x.cuda(), None if signs is None else signs.cuda())
+    torch.cuda.synchronize()
+    return codes.cpu(), exps.cpu()
+
+
+def check_quantizer(x, signs, label):
+    gc, ge = gpu_quantize(x, signs)
+    rc, re_ = F.quantize_blocks(x.float().numpy(), None if signs is None else signs.numpy())
+    same_e = np.array_equal(ge.numpy(), re_)
+    diff = int((gc.numpy() != rc).sum())
+    say(f"[quant] {label}: exponent blocks {re_.size} equal={same_e}, codes differing {diff} of {rc.size}")
+    assert same_e, "block exponents differ from the oracle"
+    assert diff == 0, "codes differ from the oracle"
+
+
+@pytest.mark.parametrize("rotate", [False, True])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (2, 150, 3), (1, 64, 2), (1, 1000, 4)])
+def test_quantizer_matches_oracle(shape, rotate):
+    B, N, H = shape
+    say(f"case quantize shape={shape} rotate={rotate}")
+    x = W.outlier_inputs(B, N, H, H, 128, seed=N + H, growth=0.5)[0]
+    signs = W.random_signs(128, seed=N) if rotate else None
+    check_quantizer(x, signs, f"{shape} rotate={rotate}")
+
+
+def test_quantizer_edge_values():
+    """An all-zero block (exponent -127), tiny values (e4m3 subnormals),
+    values at a power-of-two boundary, and values far above 448."""
+    say("case quantize edge values")
+    x = torch.zeros((1, 256, 1, 128))
+    x[0, 64:128] = torch.randn(64, 1, 128) * 1e-6
+    x[0, 128:192] = 448.0 * 2.0 ** 5
+    x[0, 130, 0, 7] = 448.0 * 2.0 ** 5 * 1.75
+    x[0, 192:256] = torch.randn(64, 1, 128) * 3e4
+    x = x.to(torch.bfloat16)
+    for signs in (None, W.random_signs(128, 3)):
+        check_quantizer(x, signs, f"edge rotate={signs is not None}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 63, 64, 65, 300])
+def test_block_attention_small(N, causal):
+    say(f"case fp8-block N={N} causal={causal}")
+    qc, qe = W.random_block_codes(2, N, 4, 128, seed=N)
+    kc, ke = W.random_block_codes(2, N, 2, 128, seed=N + 100)
+    vc, ve = W.random_block_codes(2, N, 2, 128, seed=N + 200)
+    scale = 1 / math.sqrt(128)
+    o, lse = fa.fwd_fp8_block(qc.cuda(), kc.cuda(), vc.cuda(), qe.cuda(), ke.cuda(), ve.cuda(), causal=causal,
+                              scale=scale)
+    torch.cuda.synchronize()
+    q, k, v = dequantize_blocks_f32(qc, qe), dequantize_blocks_f32(kc, ke), dequantize_blocks_f32(vc, ve)
+    compare_fp8_real(q, k, v, causal, scale, o.cpu(), lse.cpu(), label=f"block N={N} causal={causal}")
+
+
+def test_block_attention_wide_exponents():
+    """Exponents spread over -40 .. 20 (the block scales span 2^60)."""
+    say("case fp8-block wide exponents")
+    N = 333
+    qc, qe = W.random_block_codes(1, N, 2, 128, seed=1, exp_range=(-20, 0))
+    kc, ke = W.random_block_codes(1, N, 1, 128, seed=2, exp_range=(-8, 6))
+    vc, ve = W.random_block_codes(1, N, 1, 128, seed=3, exp_range=(-40, 20))
+    for causal in (False, True):
+        o, lse = fa.fwd_fp8_block(qc.cuda(), kc.cuda(), vc.cuda(), qe.cuda(), ke.cuda(), ve.cuda(),
+                                  causal=causal, scale=0.3)
+        torch.cuda.synchronize()
+        q, k, v = dequantize_blocks_f32(qc, qe), dequantize_blocks_f32(kc, ke), dequantize_blocks_f32(vc, ve)
+        compare_fp8_real(q, k, v, causal, 0.3, o.cpu(), lse.cpu(), label=f"wide exps causal={causal}")
+
+
+def test_block_attention_headline_shape():
+    """B=2, H=32, N=4096, causal, d=128, with the rotation: bf16 randn inputs
+    quantised by the oracle (q and k rotated), the library's quantiser held
+    to the same codes, the attention checked on 512 rows per head."""
+    w = W.FP8_WORKLOADS["causal_fp8_B2_H32_N4096_d128"]
+    say(f"case fp8-block {w.name}")
+    q, k, v = W.gen_inputs(W.make(w.B, w.Hq, w.Hkv, w.N, w.d, "bf16", True, seed=w.seed, name="fp8blk"))
+    signs = W.random_signs(128, seed=w.seed)
+    (qc, qe) = F.quantize_blocks(q.float().numpy(), signs.numpy())
+    (kc, ke) = F.quantize_blocks(k.float().numpy(), signs.numpy())
+    (vc, ve) = F.quantize_blocks(v.float().numpy(), None)
+    for x, sg, rc, re_, nm in ((q, signs, qc, qe, "q"), (k, signs, kc, ke, "k"), (v, None, vc, ve, "v")):
+        gc, ge = gpu_quantize(x, sg)
+        assert np.array_equal(ge.numpy(), re_), f"{nm}: exponents differ"
+        assert int((gc.numpy() != rc).sum()) == 0, f"{nm}: codes differ"
+    t = [torch.from_numpy(a) for a in (qc, kc, vc, qe, ke, ve)]
+    scale = w.scale / 128          # both q and k rotated: every score is 128 times larger
+    o, lse = fa.fwd_fp8_block(*(a.cuda() for a in t), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    qd, kd, vd = dequantize_blocks_f32(t[0], t[3]), dequantize_blocks_f32(t[1], t[4]), dequantize_blocks_f32(t[2], t[5])
+    compare_fp8_real(qd, kd, vd, True, scale, o.cpu(), lse.cpu(), rows=W.sample_rows(w), label=w.name + " block")
+
+
+def _fp8_errors(q, k, v, signs, causal=True):
+    """Mean relative row error ||o_i - O_i|| / ||O_i|| against exact attention
+    on the unquantised inputs, for one scale per (batch, head) (fa_fwd_fp8),
+    per-block scales (fa_fwd_fp8_block) and per-block scales with the rotation
+    of q and k."""
+    B, N, Hq, d = q.shape
+    scale = 1 / math.sqrt(d)
+    rows = np.array([(b, h, i) for b in range(B) for h in range(Hq) for i in range(0, N, 5)])
+    ro, _ = oracle.attention(q, k, v, scale, causal, rows=rows)
+
+    def err(o):
+        go = o.float().cpu().numpy()[rows[:, 0], rows[:, 2], rows[:, 1]].astype(np.float64)
+        return float(np.mean(np.linalg.norm(go - ro, axis=1) / np.linalg.norm(ro, axis=1)))
+
+    (q8, qd), (k8, kd), (v8, vd) = W.quantize_fp8(q.float()), W.quantize_fp8(k.float()), W.quantize_fp8(v.float())
+    o_head, _ = fa.fwd_fp8(q8.cuda(), k8.cuda(), v8.cuda(), qd.cuda(), kd.cuda(), vd.cuda(), causal=causal,
+                           scale=scale)
+    res = {}
+    for name, sg in (("block", None), ("rotated", signs.cuda())):
+        (qc, qe), (kc, ke) = fa.quantize_fp8(q.cuda(), sg), fa.quantize_fp8(k.cuda(), sg)
+        vc, ve = fa.quantize_fp8(v.cuda(), None)
+        res[name], _ = fa.fwd_fp8_block(qc, kc, vc, qe, ke, ve, causal=causal,
+                                        scale=scale / d if sg is not None else scale)
+    torch.cuda.synchronize()
+    return err(o_head), err(res["block"]), err(res["rotated"])
+
+
+def test_block_scales_keep_precision_where_magnitudes_grow():
+    """Magnitudes that grow along the sequence (each 64-row block 4x the one
+    before): one scale per (batch, head) is set by the last, largest block, so
+    the first blocks fall below e4m3's range, and the early causal rows, which
+    see only them, lose their precision; per-block scales keep it (second
+    page, section 12.2: per-block scales are more stable than per-tensor)."""
+    q, k, v = W.outlier_inputs(1, 1024, 8, 2, 128, seed=31, channels=0, growth=2.0)
+    e_head, e_block, e_rot = _fp8_errors(q, k, v, W.random_signs(128, 32))
+    say(f"[fp8 error] growing magnitudes, mean row rel err: per (b,h) {e_head:.3e}, per block {e_block:.3e}, "
+        f"per block + rotation {e_rot:.3e}")
+    assert e_block * 4 < e_head
+
+
+def test_rotation_reduces_the_error_of_outlier_features():
+    """Outlier coordinates shared by q and k (30x in 2 of 128 channels): their
+    products dominate the scores and carry the e4m3 rounding of both factors;
+    the rotation spreads them over all coordinates first (second page,
+    section 10: incoherent processing), and the error falls."""
+    q, k, v = W.outlier_inputs(1, 1024, 8, 2, 128, seed=21, channels=2, shared_channels=True)
+    e_head, e_block, e_rot = _fp8_errors(q, k, v, W.random_signs(128, 22))
+    say(f"[fp8 error] shared outlier channels, mean row rel err: per (b,h) {e_head:.3e}, per block {e_block:.3e}, "
+        f"per block + rotation {e_rot:.3e}")
+    assert e_rot * 2 < e_block
+
+
+def test_rotation_error_report_other_outliers():
+    """Two further regimes, reported (not asserted; the design doc records them):
+    rare large outliers (the rotation helps a little) and outlier channels
+    that differ between q and k (it can hurt: spreading both over all
+    coordinates enlarges the sum of squared products that the rounding
+    errors scale with)."""
+    for label, kw in (("rare outliers p=0.001", dict(channels=0, rare=0.001)),
+                      ("separate q / k outlier channels", dict(channels=2, shared_channels=False))):
+        q, k, v = W.outlier_inputs(1, 1024, 8, 2, 128, seed=41, **kw)
+        e_head, e_block, e_rot = _fp8_errors(q, k, v, W.random_signs(128, 42))
+        say(f"[fp8 error] {label}, mean row rel err: per (b,h) {e_head:.3e}, per block {e_block:.3e}, "
+            f"per block + rotation {e_rot:.3e}")
