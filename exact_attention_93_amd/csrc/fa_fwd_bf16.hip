@@ -259,7 +259,7 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     const int lq = lane & 31, hf = lane >> 5;
     const int Nq = p.Nq, Nk = p.Nk, off = p.off;
     const int q_first = tile * kBM;
-    const int wq0 = q_first + wave * 32;          // first query row of this wavefront
+    const int wq0 = __builtin_amdgcn_readfirstlane(q_first + wave * 32);   // first query row of this wavefront
     const int my_q = wq0 + lq;                    // query row owned by this lane
     const float c = p.c;
 
