@@ -29,7 +29,7 @@ import os
 
 from ._build import LIB_PATH
 
-__all__ = ["fwd", "fwd_blocksparse", "fa_fwd_blocksparse", "fwd_fp8", "fa_fwd_fp8", "fwd_fp8_block",
+__all__ = ["fwd", "fa_fwd_splitkv_static", "fwd_blocksparse", "fa_fwd_blocksparse", "fwd_fp8", "fa_fwd_fp8", "fwd_fp8_block",
            "fa_fwd_fp8_block", "quantize_fp8", "fa_quantize_fp8", "bwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_splitkv_num_splits",
            "fa_splitkv_workspace_size", "fa_strerror", "fa_version", "load_library", "FAError",
            "STATUS", "EXPORTS"]
@@ -37,9 +37,11 @@ __all__ = ["fwd", "fwd_blocksparse", "fa_fwd_blocksparse", "fwd_fp8", "fa_fwd_fp
 STATUS = {
     "FA_OK": 0, "FA_ERR_NULL": 1, "FA_ERR_SHAPE": 2, "FA_ERR_HEADS": 3, "FA_ERR_HEADDIM": 4,
     "FA_ERR_ALIGN": 5, "FA_ERR_SCALE": 6, "FA_ERR_ALIAS": 7, "FA_ERR_LAUNCH": 8,
-    "FA_ERR_SPLITS": 9, "FA_ERR_WORKSPACE": 10,
+    "FA_ERR_SPLITS": 9, "FA_ERR_WORKSPACE": 10, "FA_ERR_SCRATCH": 11,
 }
-EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_splitkv_num_splits",
+STATIC_SCRATCH_BYTES = 32 << 20   # FA_STATIC_SCRATCH_BYTES
+EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_fwd_splitkv_static",
+           "fa_splitkv_num_splits",
            "fa_splitkv_workspace_size", "fa_fwd_blocksparse", "fa_fwd_fp8", "fa_fwd_fp8_block", "fa_quantize_fp8",
            "fa_bwd", "fa_bwd_workspace_size", "fa_strerror", "fa_version")
 
@@ -73,6 +75,9 @@ def load_library(path: str = LIB_PATH):
         f = getattr(lib, name)
         f.restype = ctypes.c_int
         f.argtypes = sargs
+    lib.fa_fwd_splitkv_static.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_static.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 +
+                                          [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p])
     lib.fa_splitkv_num_splits.restype = ctypes.c_int
     lib.fa_splitkv_num_splits.argtypes = [ctypes.c_int] * 7
     lib.fa_splitkv_workspace_size.restype = ctypes.c_size_t
@@ -151,6 +156,12 @@ def fa_fwd_splitkv_f32(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, nu
                        stream) -> int:
     return load_library().fa_fwd_splitkv_f32(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, float(scale), int(causal),
                                              int(num_splits), ws, ws_bytes, stream)
+
+
+def fa_fwd_splitkv_static(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, num_splits, stream) -> int:
+    """fa_fwd_splitkv with the library's static scratch array (allocates nothing)."""
+    return load_library().fa_fwd_splitkv_static(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, float(scale), int(causal),
+                                                int(num_splits), stream)
 
 
 def fa_splitkv_num_splits(B, Hq, Hkv, Nq, Nk, d, num_splits) -> int:

@@ -72,7 +72,7 @@ size_t workspace_bytes_for(int B, int Hq, int Nq, int d, int nsplit)
 int validate_and_fill(const void *q, const void *k, const void *v, void *o, float *lse,
                       int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                       int num_splits, void *ws, size_t ws_bytes, size_t elem, fa::FwdParams &p,
-                      size_t out_elem = 0, bool allow_d256 = false)
+                      size_t out_elem = 0, bool allow_d256 = false, bool defer_ws = false)
 {
     if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
     if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
@@ -109,7 +109,7 @@ int validate_and_fill(const void *q, const void *k, const void *v, void *o, floa
     p.q_exp = p.k_exp = p.v_exp = nullptr;
     p.block_mask = nullptr;
     p.mask_nqb = p.mask_nkb = 0;
-    if (nsplit > 1) {
+    if (nsplit > 1 && !defer_ws) {
         const size_t need = workspace_bytes_for(B, Hq, Nq, d, nsplit);
         if (!ws || ws_bytes < need || ((uintptr_t)ws & 15)) return FA_ERR_WORKSPACE;
         if (overlaps(ws, need, q, nq) || overlaps(ws, need, k, nk) || overlaps(ws, need, v, nk) ||
@@ -164,6 +164,30 @@ int run(const fa::FwdParams &p, int d, bool bf16, hipStream_t stream)
 }
 
 }  // namespace
+
+namespace fa {
+
+int splitkv_prepare(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv,
+                    int Nq, int Nk, int d, float scale, int causal, int num_splits, FwdParams &p,
+                    size_t &ws_need)
+{
+    const int st = validate_and_fill(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, num_splits,
+                                     nullptr, 0, 2, p, 0, true, true);
+    if (st != FA_OK) return st;
+    ws_need = p.nsplit > 1 ? workspace_bytes_for(B, Hq, Nq, d, p.nsplit) : 0;
+    return FA_OK;
+}
+
+int splitkv_run(FwdParams &p, int d, void *ws, hipStream_t stream)
+{
+    if (p.nsplit > 1) {
+        p.o_part = (float *)ws;
+        p.lse_part = (float *)ws + (size_t)p.nsplit * p.B * p.Hq * p.Nq * (size_t)d;
+    }
+    return run(p, d, true, stream);
+}
+
+}  // namespace fa
 
 extern "C" {
 
@@ -383,6 +407,7 @@ const char *fa_strerror(int status)
     case FA_ERR_LAUNCH: return "the HIP runtime reported an error for the kernel launch";
     case FA_ERR_SPLITS: return "num_splits must be in 0..256";
     case FA_ERR_WORKSPACE: return "workspace missing or smaller than the size function returns (split forward: also 16-byte aligned)";
+    case FA_ERR_SCRATCH: return "the split forward needs more scratch memory than the library's static array holds";
     default: return "unknown fa_status";
     }
 }

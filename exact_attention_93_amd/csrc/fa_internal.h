@@ -82,6 +82,15 @@ struct QuantParams {
 };
 hipError_t launch_quant_fp8(const QuantParams &p, hipStream_t stream);
 
+// The bf16 split forward in two parts (fa_api.cpp), for entry points that
+// bring their own scratch memory: validation of every argument and the
+// workspace size it needs (0 without a split), then the launches with the
+// workspace at ws.
+int splitkv_prepare(const void *q, const void *k, const void *v, void *o, float *lse, int B, int Hq, int Hkv,
+                    int Nq, int Nk, int d, float scale, int causal, int num_splits, FwdParams &p,
+                    size_t &ws_need);
+int splitkv_run(FwdParams &p, int d, void *ws, hipStream_t stream);
+
 // Merge of the nsplit partial results into o (bf16 when out_bf16, else fp32) and lse.
 hipError_t launch_combine(const FwdParams &p, int d, int out_bf16, hipStream_t stream);
 

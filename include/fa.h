@@ -73,7 +73,8 @@ typedef enum {
     FA_ERR_ALIAS = 7,    /* o or lse overlaps q, k, v or each other              */
     FA_ERR_LAUNCH = 8,   /* the HIP runtime reported an error for the launch     */
     FA_ERR_SPLITS = 9,   /* num_splits outside 0..256                            */
-    FA_ERR_WORKSPACE = 10 /* split forward: workspace NULL, too small or not 16-byte aligned */
+    FA_ERR_WORKSPACE = 10, /* split forward: workspace NULL, too small or not 16-byte aligned */
+    FA_ERR_SCRATCH = 11  /* fa_fwd_splitkv_static: the split needs more than FA_STATIC_SCRATCH_BYTES */
 } fa_status;
 
 /*
@@ -133,6 +134,26 @@ int fa_fwd_splitkv_f32(const float *q, const float *k, const float *v, float *o,
                        float *lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
                        float scale, int causal, int num_splits, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/*
+ * fa_fwd_splitkv_static -- fa_fwd_splitkv for callers that cannot allocate
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same operation, arguments and kernels, but the
+ * per-range partial results go to a static device array of the library,
+ * FA_STATIC_SCRATCH_BYTES long, instead of a caller workspace.  The call
+ * allocates nothing.  Each GPU holds its own array until the process ends;
+ * its device address is looked up (hipGetSymbolAddress) on the first call
+ * on that device.  Every call on one GPU shares that array, so calls that
+ * overlap in time on one GPU race: enqueue them on one stream.  Returns
+ * FA_ERR_SCRATCH, before any HIP call, when the split needs more scratch
+ * than the array holds (fa_splitkv_workspace_size tells how much it needs);
+ * FA_ERR_LAUNCH if the array's address cannot be obtained.  Other errors as
+ * fa_fwd_splitkv.
+ */
+#define FA_STATIC_SCRATCH_BYTES (32u << 20)
+int fa_fwd_splitkv_static(const void *q, const void *k, const void *v, void *o, float *lse,
+                          int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                          int causal, int num_splits, void *stream);
 
 /*
  * Number of key ranges fa_fwd_splitkv uses for these arguments (num_splits

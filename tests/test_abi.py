@@ -47,7 +47,7 @@ def test_status_codes_match_header():
 
 def test_version_and_strerror(lib):
     assert fa.fa_version() == 200
-    for st in range(11):
+    for st in range(12):
         assert fa.fa_strerror(st)
     assert "unknown" in fa.fa_strerror(99)
 
