@@ -65,7 +65,7 @@ def kernel_sources(w, bwd: bool):
     shared internal header, the C-ABI layer and the public header."""
     if bwd:
         kern = ["fa_bwd_bf16.hip"]
-    elif w.dtype == "fp8":
+    elif w.dtype in ("fp8", "fp8blk"):
         kern = ["fa_fwd_fp8.hip"]
     elif w.dtype == "fp32":
         kern = ["fa_fwd_f32.hip", "fa_combine.hip"]
@@ -95,7 +95,7 @@ def traffic_file(w, bwd: bool):
         return os.path.join(PROFILES, "fa_fwd_bf16_causal_B2_H32_N4096_d128_traffic.txt")
     if w.name.startswith("decode_"):
         return os.path.join(PROFILES, f"fa_decode_bf16_{w.name}_traffic.txt")
-    kern = {"fp8": "fwd_fp8", "fp32": "fwd_f32"}.get(w.dtype, "fwd_bf16")
+    kern = {"fp8": "fwd_fp8", "fp8blk": "fwd_fp8", "fp32": "fwd_f32"}.get(w.dtype, "fwd_bf16")
     return os.path.join(PROFILES, f"fa_{kern}_{w.name}_traffic.txt")
 
 
@@ -132,9 +132,20 @@ def cpu_baseline(w, seconds: float, hbm: bool):
     import oracle
     from exact_attention_93_amd import workloads as W
 
+    scale = w.scale
     if w.dtype == "fp8":
         q8, k8, v8, qd, kd, vd = W.gen_inputs_fp8(w)
         q, k, v = W.dequantize_fp8(q8, qd), W.dequantize_fp8(k8, kd), W.dequantize_fp8(v8, vd)
+    elif w.dtype == "fp8blk":
+        # the oracle's block quantiser (q and k rotated), then the real values
+        import torch
+        from oracle import fp8 as F
+        qb, kb, vb = W.gen_inputs(w)
+        signs = W.random_signs(w.d, w.seed).numpy()
+        deq = lambda x, sg: torch.from_numpy(F.dequantize_blocks(*F.quantize_blocks(x.float().numpy(), sg))
+                                             .astype(np.float32))
+        q, k, v = deq(qb, signs), deq(kb, signs), deq(vb, None)
+        scale = w.scale / w.d
     else:
         q, k, v = W.gen_inputs(w)
     bb, hh, ii = np.meshgrid(np.arange(w.B), np.arange(w.Hq), np.arange(w.N), indexing="ij")
@@ -147,12 +158,12 @@ def cpu_baseline(w, seconds: float, hbm: bool):
         mk = {"block_mask": w.block_mask(), "block": (128, 64)}
     probe = rows[np.linspace(0, len(rows) - 1, min(1024, len(rows))).astype(int)]
     t0 = time.perf_counter()
-    oracle.attention(q, k, v, w.scale, w.causal, rows=probe, threads=threads, **mk)
+    oracle.attention(q, k, v, scale, w.causal, rows=probe, threads=threads, **mk)
     dt = max(time.perf_counter() - t0, 1e-3)
     n = int(min(len(rows), max(len(probe), len(probe) * seconds / dt)))
     pick = rows[np.linspace(0, len(rows) - 1, n).astype(int)]
     t0 = time.perf_counter()
-    oracle.attention(q, k, v, w.scale, w.causal, rows=pick, threads=threads, **mk)
+    oracle.attention(q, k, v, scale, w.causal, rows=pick, threads=threads, **mk)
     dt = time.perf_counter() - t0
     sample = (f"all {n} query rows of {w.name}" if n == len(rows) else
               f"{n} of the {len(rows)} query rows of {w.name}, evenly strided over (b, h, i)")
@@ -173,7 +184,7 @@ def cpu_baseline(w, seconds: float, hbm: bool):
     # The same oracle on one thread, over every `threads`-th row of the sample.
     one = pick[::threads]
     t0 = time.perf_counter()
-    oracle.attention(q, k, v, w.scale, w.causal, rows=one, threads=1, **mk)
+    oracle.attention(q, k, v, scale, w.causal, rows=one, threads=1, **mk)
     dt1 = time.perf_counter() - t0
     scale_unit, unit = (1e9, "GB/s") if hbm else (1e12, "TFLOP/s")
     what = ("bytes counted as the sample's share of the workload's algorithmic bytes" if hbm
@@ -238,8 +249,16 @@ def main():
 
     w = W.ALL_WORKLOADS[args.workload or W.HEADLINE]
     dev = torch.device("cuda:0")
-    fp8 = w.dtype == "fp8"
-    if fp8:
+    fp8 = w.dtype in ("fp8", "fp8blk")
+    fp8blk = w.dtype == "fp8blk"
+    if fp8blk:
+        # block-scaled e4m3 inputs from the library's own quantiser (q and k rotated)
+        qb, kb, vb = (t.to(dev) for t in W.gen_inputs(w))
+        signs = W.random_signs(w.d, w.seed).to(dev)
+        (q, qd), (k, kd) = fa.quantize_fp8(qb, signs), fa.quantize_fp8(kb, signs)
+        v, vd = fa.quantize_fp8(vb, None)
+        o = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=dev)
+    elif fp8:
         q, k, v, qd, kd, vd = (t.to(dev) for t in W.gen_inputs_fp8(w))
         o = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=dev)
     else:
@@ -292,6 +311,10 @@ def main():
         fa.fwd_blocksparse(q, k, v, bmask, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
         entry, cargs = lib.fa_fwd_blocksparse, (ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), w.B, w.Hq, w.Hkv, w.N,
                                                 w.d, w.scale, int(w.causal), ptr(bmask), sp)
+    elif fp8blk:
+        fa.fwd_fp8_block(q, k, v, qd, kd, vd, causal=w.causal, scale=w.scale / w.d, out=o, lse=lse, stream=stream)
+        entry, cargs = lib.fa_fwd_fp8_block, (ptr(q), ptr(k), ptr(v), ptr(qd), ptr(kd), ptr(vd), ptr(o), ptr(lse),
+                                              w.B, w.Hq, w.Hkv, w.N, w.d, w.scale / w.d, int(w.causal), sp)
     elif fp8:
         fa.fwd_fp8(q, k, v, qd, kd, vd, causal=w.causal, scale=w.scale, out=o, lse=lse, stream=stream)
         entry, cargs = lib.fa_fwd_fp8, (ptr(q), ptr(k), ptr(v), ptr(qd), ptr(kd), ptr(vd), ptr(o), ptr(lse),
@@ -383,6 +406,9 @@ def main():
     traffic = read_traffic(traffic_file(w, bwd), src_hash)
     if bwd:
         metric = f"attn bwd TFLOP/s (2.5x forward FLOPs) on {w.name}; % of dense bf16 MFMA peak"
+    elif fp8blk:
+        metric = (f"attn fwd TFLOP/s on {w.name} (e4m3 inputs with one power-of-two scale per 64 rows, q and k "
+                  "Hadamard-rotated; bf16 output); % of dense fp8 MFMA peak")
     elif fp8:
         metric = f"attn fwd TFLOP/s on {w.name} (e4m3 inputs, bf16 output); % of dense fp8 MFMA peak"
     elif sparse:
@@ -432,6 +458,11 @@ def main():
         out["dtype"] = "fp8-e4m3"
         out["data"] = "synthetic (seeded randn, e4m3 round-to-nearest-even with one scale per (batch, head))"
         out["config"].update({"io_dtype": "e4m3 in, bf16 out", "descale": "per (batch, head)"})
+    if fp8blk:
+        out["data"] = ("synthetic (seeded randn in bf16, quantised on the GPU by fa_quantize_fp8: q and k "
+                       "rotated by a seeded random-sign Hadamard transform, one power-of-two scale per 64 rows)")
+        out["config"].update({"descale": "per 64-row block (power of two)", "rotation": "q, k: random-sign Hadamard",
+                              "scale_passed": w.scale / w.d})
     if args.cpu_seconds > 0:
         out["cpu_baseline"] = (cpu_baseline_bwd(w, args.cpu_seconds, do_host) if bwd
                                else cpu_baseline(w, args.cpu_seconds, hbm_bound))

@@ -79,7 +79,7 @@ class Workload:
     def io_bytes(self) -> int:
         """Bytes the forward must move at least once: q, k, v read, o and lse written
         (fp8: one-byte inputs, bf16 output)."""
-        s_in = {"fp32": 4, "fp8": 1}.get(self.dtype, 2)
+        s_in = {"fp32": 4, "fp8": 1, "fp8blk": 1}.get(self.dtype, 2)
         s_out = 4 if self.dtype == "fp32" else 2
         return ((self.Hq * self.N * (s_in + s_out) + 2 * self.Hkv * self.Nkv * s_in) * self.B * self.d
                 + 4 * self.B * self.Hq * self.N)
@@ -113,6 +113,10 @@ SPLIT_WORKLOADS = {
 FP8_WORKLOADS = {
     "causal_fp8_B2_H32_N4096_d128": Workload(
         "causal_fp8_B2_H32_N4096_d128", 2, 32, 32, 4096, 128, "fp8", True, 1.0, 1008),
+    # the same shape with block-scaled e4m3 inputs: the seeded bf16 draws of
+    # gen_inputs, with q and k rotated by random_signs(128, seed)
+    "causal_fp8blk_B2_H32_N4096_d128": Workload(
+        "causal_fp8blk_B2_H32_N4096_d128", 2, 32, 32, 4096, 128, "fp8blk", True, 1.0, 1011),
 }
 # Head dimension 256 (the FLOP count of the headline case, half the heads).
 D256_WORKLOADS = {
@@ -175,7 +179,7 @@ def gen_inputs(w: Workload):
     v = torch.randn((w.B, w.Nkv, w.Hkv, w.d), generator=g, dtype=torch.float32)
     if w.q_std != 1.0:
         q = q * w.q_std
-    if w.dtype == "bf16":
+    if w.dtype in ("bf16", "fp8blk"):     # fp8blk: the bf16 values its quantiser starts from
         q, k, v = q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16)
     elif w.dtype != "fp32":
         raise ValueError(w.dtype)

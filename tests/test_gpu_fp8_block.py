@@ -93,9 +93,9 @@ def test_block_attention_headline_shape():
     """B=2, H=32, N=4096, causal, d=128, with the rotation: bf16 randn inputs
     quantised by the oracle (q and k rotated), the library's quantiser held
     to the same codes, the attention checked on 512 rows per head."""
-    w = W.FP8_WORKLOADS["causal_fp8_B2_H32_N4096_d128"]
+    w = W.FP8_WORKLOADS["causal_fp8blk_B2_H32_N4096_d128"]
     say(f"case fp8-block {w.name}")
-    q, k, v = W.gen_inputs(W.make(w.B, w.Hq, w.Hkv, w.N, w.d, "bf16", True, seed=w.seed, name="fp8blk"))
+    q, k, v = W.gen_inputs(w)
     signs = W.random_signs(128, seed=w.seed)
     (qc, qe) = F.quantize_blocks(q.float().numpy(), signs.numpy())
     (kc, ke) = F.quantize_blocks(k.float().numpy(), signs.numpy())
@@ -109,7 +109,7 @@ def test_block_attention_headline_shape():
     o, lse = fa.fwd_fp8_block(*(a.cuda() for a in t), causal=True, scale=scale)
     torch.cuda.synchronize()
     qd, kd, vd = dequantize_blocks_f32(t[0], t[3]), dequantize_blocks_f32(t[1], t[4]), dequantize_blocks_f32(t[2], t[5])
-    compare_fp8_real(qd, kd, vd, True, scale, o.cpu(), lse.cpu(), rows=W.sample_rows(w), label=w.name + " block")
+    compare_fp8_real(qd, kd, vd, True, scale, o.cpu(), lse.cpu(), rows=W.sample_rows(w), label=w.name)
 
 
 def _fp8_errors(q, k, v, signs, causal=True):
