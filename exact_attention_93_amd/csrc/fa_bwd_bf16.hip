@@ -39,6 +39,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
 #include <type_traits>
 
 #include "fa_internal.h"
@@ -107,6 +108,14 @@ __device__ __forceinline__ void load_lds4(const void *base, int range, uint32_t 
 __device__ __forceinline__ void vm_wait_all()
 {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// A scheduling group of n LDS reads (n in 0..3, known once loops are unrolled).
+__device__ __forceinline__ void ds_group(int n)
+{
+    if (n >= 3) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    else if (n == 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    else if (n == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 }
 
 // A rows of the first two products: bits 2 and 3 of the lane's row swapped.
@@ -353,20 +362,36 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p)
 }
 
 // ====================================================== dK, dV (K/V-outer)
+// One wavefront per SIMD, so the overlap of matrix products, vector-ALU
+// softmax work and LDS operand reads has to come from within the wavefront.
+// Each query tile (two 32-row blocks) runs as four stages, each a run of
+// products with other work placed between them:
+//   A: S0, dP0            | row operands of block 1, lse/delta of block 0
+//   B: S1, dP1            | softmax of block 0, transposed operands of block 0
+//   C: dV += dO0^T P0 ... | softmax of block 1, transposed operands of block 1
+//   D: dV, dK of block 1  | row operands of block 0 of the next tile
+// The tile's synchronisation (its data resident, the previous buffer free)
+// sits between C and D, so D's reads already come from the next tile.
 template <int D, bool CAUSAL>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p)
 {
     constexpr int BN = 128, BQ = 64;     // keys per workgroup, query rows per tile
-    constexpr int KSTEPS = D / 16, XB = D / 32, NQB = BQ / 32;
+    constexpr int KSTEPS = D / 16, XB = D / 32;
     constexpr int CHUNKS = D / 8, ROW_BYTES = D * 2, ROWS_PER_BLK = 1024 / ROW_BYTES;
     constexpr int BLKS = BQ * ROW_BYTES / 1024, BLKS_PER_WAVE = BLKS / 4;
-    constexpr int TILE = BQ * D;
-
-    __shared__ __attribute__((aligned(1024))) uint16_t Qs0[TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t Qs1[TILE];
-    __shared__ __attribute__((aligned(1024))) uint16_t Os0[TILE];   // dO
-    __shared__ __attribute__((aligned(1024))) uint16_t Os1[TILE];
-    __shared__ __attribute__((aligned(16))) float Ls0[BQ], Ls1[BQ], Ds0[BQ], Ds1[BQ];
+    constexpr int TILE_BYTES = BQ * ROW_BYTES;
+    // Two stages of the Q tile, the dO tile and the tile's lse2 and delta,
+    // as separate arrays: a stage is always named at compile time, so the
+    // compiler sees that the loads into one stage do not touch the other
+    // and need not wait for them before reading it.
+    __shared__ __attribute__((aligned(1024))) char Qs0[TILE_BYTES], Qs1[TILE_BYTES], Os0[TILE_BYTES], Os1[TILE_BYTES];
+    // lse2 and delta: one copy per wavefront, so that every wavefront loads
+    // its own with no branch around the load
+    __shared__ __attribute__((aligned(16))) char Ls0[4 * BQ * 4], Ls1[4 * BQ * 4], Ds0[4 * BQ * 4], Ds1[4 * BQ * 4];
+    auto stage = [&](auto S) __attribute__((always_inline)) {
+        if constexpr (decltype(S)::value == 0) return std::make_tuple(Qs0, Os0, Ls0, Ds0);
+        else return std::make_tuple(Qs1, Os1, Ls1, Ds1);
+    };
 
     // (batch, K/V head, key tile); with B*Hkv a multiple of 8, every key tile
     // of a head runs on one XCD, whose L2 then serves that head's Q and dO
@@ -388,9 +413,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p)
     }
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int lk = lane & 31, hf = lane >> 5;
     const int Nq = p.Nq, Nk = p.Nk, off = p.off, G = p.group;
-    const int k_first = kt * BN, wk0 = k_first + wave * 32, my_k = wk0 + lk;
+    const int k_first = kt * BN, wk0 = k_first + wave_u * 32, my_k = wk0 + lk;
     const float c = p.c;
     const int sQ = p.Hq * D;
 
@@ -421,23 +447,37 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p)
     // ---- query tiles: causal rows i see key j iff i >= j - off
     const int q_lo = CAUSAL ? max(0, k_first - off) : 0;
     const int qt_lo = q_lo / BQ;
-    const int nqt = q_lo < Nq ? (Nq + BQ - 1) / BQ - qt_lo : 0;
-    const int total = G * nqt;            // (query head in group, query tile) pairs
-    const bool wave_live = wk0 < Nk;
+    const int qt_end = (Nq + BQ - 1) / BQ;
+    const int nqt = q_lo < Nq ? qt_end - qt_lo : 0;
+    const int total = G * nqt;            // (query head in group, query tile) pairs, in that order
+    // Per head, the tiles in [m1, m2) need no mask for this wavefront: (causal)
+    // their first row already sees all 32 of its keys, and they end inside Nq.
+    const int m2 = max(qt_lo, (Nq % BQ) != 0 ? qt_end - 1 : qt_end);
+    int m1 = qt_lo;
+    if (CAUSAL) {
+        const int need = wk0 + 31 - off;  // first row that sees every key of the wavefront
+        m1 = need <= 0 ? 0 : (need + BQ - 1) / BQ;
+        m1 = min(max(m1, qt_lo), m2);
+    }
 
     const int range = Nq * sQ * 2;
     // Per-lane byte offsets within a tile are fixed; the tile's own offset
     // goes in as the scalar offset, and the LDS destinations are uniform.
     const int ld_row = lane / CHUNKS, ld_pch = lane % CHUNKS;
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     uint32_t ld_voff[BLKS_PER_WAVE];
 #pragma unroll
     for (int i = 0; i < BLKS_PER_WAVE; ++i) {
         const int row = (wave * BLKS_PER_WAVE + i) * ROWS_PER_BLK + ld_row;
         ld_voff[i] = (uint32_t)row * (uint32_t)(sQ * 2) + ((ld_pch ^ swz<D>(row)) * 16);
     }
-    auto load = [&](int it, uint16_t *qd, uint16_t *od, float *ld, float *dd) {
-        const int hh = it / nqt, qt = qt_lo + (it - (it / nqt) * nqt);
+    // tile `it` (head hk*G + it/nqt, query tile qt_lo + it%nqt) into stage S = it&1
+    // Issued whether or not the tile exists (it >= total loads nothing: zero
+    // ranges), so that no branch separates loads from the reads after them.
+    auto load = [&](auto S, int it_) __attribute__((always_inline)) {
+        auto [qd, od, ld, dd] = stage(S);
+        const bool live = it_ < total;
+        const int it = live ? it_ : 0;
+        const int hh = it / nqt, qt = qt_lo + (it - hh * nqt);
         const int h = hk * G + hh;
         const uint16_t *qb = (const uint16_t *)p.q + ((int64_t)b * Nq * p.Hq + h) * D;
         const uint16_t *ob = (const uint16_t *)p.dout + ((int64_t)b * Nq * p.Hq + h) * D;
@@ -445,15 +485,23 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p)
 #pragma unroll
         for (int i = 0; i < BLKS_PER_WAVE; ++i) {
             const int blk = wave_u * BLKS_PER_WAVE + i;
-            load_lds16(qb, range, ld_voff[i], soff, (lds_void_t *)&qd[blk * 512]);
-            load_lds16(ob, range, ld_voff[i], soff, (lds_void_t *)&od[blk * 512]);
+            load_lds16(qb, live ? range : 0, ld_voff[i], soff, (lds_void_t *)(qd + blk * 1024));
+            load_lds16(ob, live ? range : 0, ld_voff[i], soff, (lds_void_t *)(od + blk * 1024));
         }
-        if (wave == 0) {                  // the tile's 64 lse and delta values
-            const int64_t r0 = ((int64_t)b * p.Hq + h) * Nq;
-            const int rng = max(0, Nq - qt * BQ) * 4;
-            load_lds4(p.lse2 + r0 + qt * BQ, rng, lane * 4, (lds_void_t *)ld);
-            load_lds4(p.delta + r0 + qt * BQ, rng, lane * 4, (lds_void_t *)dd);
-        }
+        // the tile's 64 lse and delta values, into this wavefront's copy
+        const int64_t r0 = ((int64_t)b * p.Hq + h) * Nq;
+        const int rng = live ? max(0, Nq - qt * BQ) * 4 : 0;
+        load_lds4(p.lse2 + r0 + qt * BQ, rng, lane * 4, (lds_void_t *)(ld + wave_u * BQ * 4));
+        load_lds4(p.delta + r0 + qt * BQ, rng, lane * 4, (lds_void_t *)(dd + wave_u * BQ * 4));
+    };
+    // Tile `it` resident and visible, every wavefront done with tile it-1's
+    // buffer; then tile it+1 goes into that buffer.  (Called once more after
+    // the last tile, so that every wavefront passes the same barriers.)
+    // S is the stage of tile it+1, the one tile it-1 used.
+    auto sync = [&](auto S, int it) __attribute__((always_inline)) {
+        vm_wait_all();
+        __syncthreads();
+        load(S, it + 1);
     };
 
     f32x16_t dk[XB], dv[XB];
@@ -461,162 +509,206 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p)
     for (int xb = 0; xb < XB; ++xb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) dk[xb][i] = dv[xb][i] = 0.f;
-    const int prow = perm_row(lk);
 
-    // One query tile (two 32-row blocks) in one basic block, in the order
-    //   S0, dP0 | softmax 0 | S1, dP1 | dV0, dK0 | softmax 1 | dV1, dK1,
-    // so that the compiler can run each softmax (vector ALU) under the
-    // neighbouring independent products (one wavefront per SIMD: overlap
-    // comes from within the wavefront).  The masked form (tiles that cross
-    // the diagonal or the end) is a separate instance.
-    auto sdp_products = [&](int qb, const char *qs, const char *os, f32x16_t &s, f32x16_t &dp)
-                            __attribute__((always_inline)) {
+    // LDS read offsets (bytes within a tile).  The chunk permutation depends
+    // on a row only through bits 0..3, which every row a lane reads shares,
+    // so block qb adds qb*32 rows and transpose group u adds 16u rows.
+    const int prow = perm_row(lk);
+    int rc_off[KSTEPS], tr_off[2][XB];
+    {
+        const int tg = lane >> 4, ts = lane & 15;
+        const int tr_row = 8 * (tg >> 1) + (ts >> 2);
+        const int tr_chunk = 2 * (tg & 1) + ((ts & 3) >> 1);
+        const int tr_byte = 8 * (ts & 1);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
+        for (int t = 0; t < KSTEPS; ++t) rc_off[t] = prow * ROW_BYTES + (((2 * t + hf) ^ swz<D>(prow)) * 16);
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int xb = 0; xb < XB; ++xb) {
+                const int rw = 4 * r + tr_row;
+                tr_off[r][xb] = rw * ROW_BYTES + (((4 * xb + tr_chunk) ^ swz<D>(rw)) * 16) + tr_byte;
+            }
+    }
+    // transposed operand A[x][k] = tile[16u + k][32xb + x] of a 32-row block
+    auto tr_read = [&](const char *blk, int u, int xb) __attribute__((always_inline)) -> u32x4_t {
+        u32x4_t a;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const i16x4_t t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4_t *)(blk + tr_off[r][xb] + 16 * u * ROW_BYTES));
+            const u32x2_t t2 = __builtin_bit_cast(u32x2_t, t4);
+            a[2 * r] = t2[0];
+            a[2 * r + 1] = t2[1];
+        }
+        return a;
+    };
+    auto row_read = [&](const char *blk, int t) __attribute__((always_inline)) -> u32x4_t {
+        return *(const u32x4_t *)(blk + rc_off[t]);
+    };
+    // lse2 and delta of the 16 rows a lane holds in a 32-row block: register i
+    // holds row 16*(i/8) + 8*hf + (i%8), so four 4-float reads each
+    auto stat_read = [&](const char *base, int qb, f32x4_t (&v)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                v[2 * u + h] = *(const f32x4_t *)(base + 4 * (qb * 32 + 16 * u + 8 * hf + 4 * h));
+    };
+    // P and dS = P (dP - delta) for the register pair (u, w) of one block
+    // (rows 16u + 8hf + 2w, +1), as bf16 B-operand words.  With MASK, rows
+    // past Nq and (causal) keys after the row's last visible key get P = 0.
+    auto softmax_pair = [&](auto MASK, int qrow0, int u, int w, const f32x16_t &s, const f32x16_t &dp,
+                            const f32x4_t (&l2)[4], const f32x4_t (&dl)[4], u32x4_t (&pb)[2], u32x4_t (&dsb)[2])
+                            __attribute__((always_inline)) {
+        constexpr bool M = decltype(MASK)::value;
+        float pv[2], dsv[2];
+#pragma unroll
+        for (int z = 0; z < 2; ++z) {
+            const int e = 2 * w + z, i = 8 * u + e;
+            float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -l2[2 * u + (e >> 2)][e & 3]));
+            if constexpr (M) {
+                // valid rows: lo <= 16u + e <= hi (register order within the block)
+                const int hi = Nq - 1 - qrow0 - 8 * hf;
+                const int lo = CAUSAL ? my_k - off - qrow0 - 8 * hf : -BQ;
+                const int re = 16 * u + e;
+                pe = ((re >= lo) & (re <= hi)) ? pe : 0.f;
+            }
+            pv[z] = pe;
+            dsv[z] = pe * (dp[i] - dl[2 * u + (e >> 2)][e & 3]);
+        }
+        pb[u][w] = pack_bf16(pv[0], pv[1]);
+        dsb[u][w] = pack_bf16(dsv[0], dsv[1]);
+    };
+
+    // Row operands of block 0 of the next tile, carried from stage D.
+    u32x4_t qa0[KSTEPS], oa0[KSTEPS];
+    auto read_block0 = [&](auto S) __attribute__((always_inline)) {
+        auto [qs, os, ls_, ds_] = stage(S);
 #pragma unroll
         for (int t = 0; t < KSTEPS; ++t) {
-            s = mfma_bf16(row_chunk<D>(qs, qb * 32 + prow, 2 * t + hf), kreg[t], s);
-            dp = mfma_bf16(row_chunk<D>(os, qb * 32 + prow, 2 * t + hf), vreg[t], dp);
+            qa0[t] = row_read(qs, t);
+            oa0[t] = row_read(os, t);
         }
     };
-    // register i holds query row qt*BQ + qb*32 + 16*(i/8) + 8*hf + (i%8)
-    auto softmax = [&](auto masked, int qt, int qb, const f32x16_t &s, const f32x16_t &dp, const float *ls,
-                       const float *dsm, u32x4_t (&pb)[2], u32x4_t (&dsb)[2]) __attribute__((always_inline)) {
-        constexpr bool MASK = decltype(masked)::value;
+
+    // One query tile.  Stages B and C are written as KSTEPS chunks, each two
+    // products with its share of the softmax and the operand reads after
+    // them, the chunks kept apart by scheduling barriers: one pair of
+    // softmax registers per chunk at d = 128, two at d = 64.
+    constexpr int NCH = KSTEPS, PAIRS = 8 / NCH, STATS = 8 / NCH;
+    static_assert(2 * XB == NCH && 4 * XB == 2 * NCH, "two transposed operands and two products per chunk");
+    // S: the tile's stage (it & 1), known at compile time.
+    auto tile = [&](auto MASK, auto S, int it, int qt) __attribute__((always_inline)) {
+        constexpr int SN = 1 - decltype(S)::value;
+        auto [qs, os, ls, ds] = stage(S);
+        // ---- A: S0, dP0 | row operands of block 1, stats of block 0
+        f32x16_t s0, dp0, s1, dp1;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int lq0 = qb * 32 + 16 * u + 8 * hf;   // first of the 8 rows in LDS order
-            const f32x4_t la = *(const f32x4_t *)&ls[lq0], lb = *(const f32x4_t *)&ls[lq0 + 4];
-            const f32x4_t da = *(const f32x4_t *)&dsm[lq0], db = *(const f32x4_t *)&dsm[lq0 + 4];
+        for (int i = 0; i < 16; ++i) s0[i] = dp0[i] = 0.f;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                float pv[2], dsv[2];
+        for (int t = 0; t < KSTEPS; ++t) {
+            s0 = mfma_bf16(qa0[t], kreg[t], s0);
+            dp0 = mfma_bf16(oa0[t], vreg[t], dp0);
+        }
+        u32x4_t qa1[KSTEPS], oa1[KSTEPS];
 #pragma unroll
-                for (int z = 0; z < 2; ++z) {
-                    const int e = 2 * w + z, i = 8 * u + e;
-                    const float l2 = e < 4 ? la[e] : lb[e - 4];
-                    const float dr = e < 4 ? da[e] : db[e - 4];
-                    float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -l2));
-                    if (MASK) {
-                        const int qi = qt * BQ + qb * 32 + 16 * u + 8 * hf + e;
-                        if (qi >= Nq || (CAUSAL && my_k > qi + off)) pe = 0.f;
-                    }
-                    pv[z] = pe;
-                    dsv[z] = pe * (dp[i] - dr);
-                }
-                pb[u][w] = pack_bf16(pv[0], pv[1]);
-                dsb[u][w] = pack_bf16(dsv[0], dsv[1]);
+        for (int t = 0; t < KSTEPS; ++t) {
+            qa1[t] = row_read(qs + 32 * ROW_BYTES, t);
+            oa1[t] = row_read(os + 32 * ROW_BYTES, t);
+        }
+        f32x4_t l20[4], dl0[4], l21[4], dl1[4];
+        stat_read(ls + wave_u * BQ * 4, 0, l20);
+        stat_read(ds + wave_u * BQ * 4, 0, dl0);
+#pragma unroll
+        for (int i = 0; i < 2 * KSTEPS; ++i) {      // 2*KSTEPS + 8 reads
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            ds_group(i < 8 ? 2 : 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // ---- B: S1, dP1 | softmax of block 0, transposed operands of block 0, stats of block 1
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s1[i] = dp1[i] = 0.f;
+        u32x4_t pb0[2], dsb0[2], to0[2][XB], tq0[2][XB];
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            s1 = mfma_bf16(qa1[t], kreg[t], s1);
+            dp1 = mfma_bf16(oa1[t], vreg[t], dp1);
+#pragma unroll
+            for (int g = PAIRS * t; g < PAIRS * (t + 1); ++g)
+                softmax_pair(MASK, qt * BQ, g >> 2, g & 3, s0, dp0, l20, dl0, pb0, dsb0);
+            const int u = t / XB, xb = t % XB;
+            to0[u][xb] = tr_read(os, u, xb);
+            tq0[u][xb] = tr_read(qs, u, xb);
+#pragma unroll
+            for (int r = STATS * t; r < STATS * (t + 1); ++r) {
+                const int h = r & 3;
+                const int o = wave_u * BQ * 4 + 4 * (32 + 16 * (h >> 1) + 8 * hf + 4 * (h & 1));
+                if (r < 4) l21[h] = *(const f32x4_t *)(ls + o);
+                else dl1[h] = *(const f32x4_t *)(ds + o);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
-    };
-    auto dvdk_products = [&](int qb, const char *qs, const char *os, const u32x4_t (&pb)[2],
-                             const u32x4_t (&dsb)[2]) __attribute__((always_inline)) {
+        // ---- C: dV, dK of block 0 | softmax of block 1, transposed operands of block 1
+        u32x4_t pb1[2], dsb1[2], to1[2][XB], tq1[2][XB];
+#pragma unroll
+        for (int t = 0; t < NCH; ++t) {
+            const int u = t / XB, xb = t % XB;
+            dv[xb] = mfma_bf16(to0[u][xb], pb0[u], dv[xb]);
+            dk[xb] = mfma_bf16(tq0[u][xb], dsb0[u], dk[xb]);
+#pragma unroll
+            for (int g = PAIRS * t; g < PAIRS * (t + 1); ++g)
+                softmax_pair(MASK, qt * BQ + 32, g >> 2, g & 3, s1, dp1, l21, dl1, pb1, dsb1);
+            to1[u][xb] = tr_read(os + 32 * ROW_BYTES, u, xb);
+            tq1[u][xb] = tr_read(qs + 32 * ROW_BYTES, u, xb);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // keep block 1's softmax here, ahead of the synchronisation below
+        asm volatile("" : "+v"(pb1[0]), "+v"(pb1[1]), "+v"(dsb1[0]), "+v"(dsb1[1]));
+        // ---- the next tile's synchronisation; then D: dV, dK of block 1 | row operands of block 0 of tile it+1
+        sync(S, it + 1);          // tile it+2 goes into this tile's stage
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
             for (int xb = 0; xb < XB; ++xb) {
-                dv[xb] = mfma_bf16(tr_operand<D>(os + qb * 32 * ROW_BYTES, u, xb, lane), pb[u], dv[xb]);
-                dk[xb] = mfma_bf16(tr_operand<D>(qs + qb * 32 * ROW_BYTES, u, xb, lane), dsb[u], dk[xb]);
+                dv[xb] = mfma_bf16(to1[u][xb], pb1[u], dv[xb]);
+                dk[xb] = mfma_bf16(tq1[u][xb], dsb1[u], dk[xb]);
             }
-    };
-    auto tile_compute = [&](auto masked, int qt, const char *qs, const char *os, const float *ls, const float *dsm)
-                            __attribute__((always_inline)) {
-        static_assert(NQB == 2, "two 32-row blocks per query tile");
-        f32x16_t s0, dp0, s1, dp1;
-        u32x4_t pb0[2], dsb0[2], pb1[2], dsb1[2];
-        sdp_products(0, qs, os, s0, dp0);
-        softmax(masked, qt, 0, s0, dp0, ls, dsm, pb0, dsb0);
-        sdp_products(1, qs, os, s1, dp1);
-        dvdk_products(0, qs, os, pb0, dsb0);
-        softmax(masked, qt, 1, s1, dp1, ls, dsm, pb1, dsb1);
-        dvdk_products(1, qs, os, pb1, dsb1);
-    };
-    // Non-causal: one 32-row block at a time (the per-tile form below makes
-    // the compiler spill at d = 128 without a causal mask).
-    auto compute_blockwise = [&](int it, const uint16_t *qs_, const uint16_t *os_, const float *ls, const float *dsm)
-                                 __attribute__((always_inline)) {
-        const int qt = qt_lo + (it - (it / nqt) * nqt);
-        const char *qs = (const char *)qs_, *os = (const char *)os_;
+        read_block0(std::integral_constant<int, SN>{});   // (after the last tile: values nobody uses)
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) {
-            const int qrow0 = qt * BQ + qb * 32;           // first query row of this block
-            if (CAUSAL && qrow0 + 31 + off < wk0) continue; // no row of the block sees a key of this wavefront
-            f32x16_t s, dp;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[i] = dp[i] = 0.f;
-            const int row = qb * 32 + prow;
-#pragma unroll
-            for (int t = 0; t < KSTEPS; ++t) {
-                s = mfma_bf16(row_chunk<D>(qs, row, 2 * t + hf), kreg[t], s);
-                dp = mfma_bf16(row_chunk<D>(os, row, 2 * t + hf), vreg[t], dp);
-            }
-            // register i holds query row qrow0 + 16*(i/8) + 8*hf + (i%8)
-            const bool need_mask = (qrow0 + 32 > Nq) || (CAUSAL && qrow0 + off < wk0 + 31);
-            u32x4_t pb[2], dsb[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int lq0 = qb * 32 + 16 * u + 8 * hf;   // first of the 8 rows in LDS order
-                const f32x4_t la = *(const f32x4_t *)&ls[lq0], lb = *(const f32x4_t *)&ls[lq0 + 4];
-                const f32x4_t da = *(const f32x4_t *)&dsm[lq0], db = *(const f32x4_t *)&dsm[lq0 + 4];
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    float pv[2], dsv[2];
-#pragma unroll
-                    for (int z = 0; z < 2; ++z) {
-                        const int e = 2 * w + z, i = 8 * u + e;
-                        const float lr = e < 4 ? la[e] : lb[e - 4];
-                        const float dr = e < 4 ? da[e] : db[e - 4];
-                        const float l2 = lr;   // already lse * log2(e), +inf for rows without keys
-                        float pe = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -l2));
-                        if (need_mask) {
-                            const int qi = qrow0 + 16 * u + 8 * hf + e;
-                            if (qi >= Nq || (CAUSAL && my_k > qi + off)) pe = 0.f;
-                        }
-                        pv[z] = pe;
-                        dsv[z] = pe * (dp[i] - dr);
-                    }
-                    pb[u][w] = pack_bf16(pv[0], pv[1]);
-                    dsb[u][w] = pack_bf16(dsv[0], dsv[1]);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int xb = 0; xb < XB; ++xb) {
-                    dv[xb] = mfma_bf16(tr_operand<D>(os + qb * 32 * ROW_BYTES, u, xb, lane), pb[u], dv[xb]);
-                    dk[xb] = mfma_bf16(tr_operand<D>(qs + qb * 32 * ROW_BYTES, u, xb, lane), dsb[u], dk[xb]);
-                }
+        for (int i = 0; i < 2 * NCH; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
     };
 
-    auto compute = [&](int it, const uint16_t *qs_, const uint16_t *os_, const float *ls, const float *dsm)
-                       __attribute__((always_inline)) {
-        const int qt = qt_lo + (it - (it / nqt) * nqt);
-        const int qrow0 = qt * BQ;
-        // some (row, key) pair of this wavefront is masked: a row past the
-        // end, or (causal) the tile's first row sees fewer than all keys
-        const bool need_mask = (qrow0 + BQ > Nq) || (CAUSAL && qrow0 + off < wk0 + 31);
-        if (need_mask) tile_compute(std::true_type{}, qt, (const char *)qs_, (const char *)os_, ls, dsm);
-        else tile_compute(std::false_type{}, qt, (const char *)qs_, (const char *)os_, ls, dsm);
-    };
-    auto step = [&](int it, const uint16_t *qs_, const uint16_t *os_, const float *ls, const float *dsm)
-                    __attribute__((always_inline)) {
-        if constexpr (CAUSAL) compute(it, qs_, os_, ls, dsm);
-        else compute_blockwise(it, qs_, os_, ls, dsm);
-    };
-
-    if (total > 0) load(0, Qs0, Os0, Ls0, Ds0);
-    for (int it = 0; it < total; it += 2) {
-        vm_wait_all();
-        __syncthreads();
-        if (it + 1 < total) load(it + 1, Qs1, Os1, Ls1, Ds1);
-        if (wave_live) step(it, Qs0, Os0, Ls0, Ds0);
-        if (it + 1 < total) {
-            vm_wait_all();
-            __syncthreads();
-            if (it + 2 < total) load(it + 2, Qs0, Os0, Ls0, Ds0);
-            if (wave_live) step(it + 1, Qs1, Os1, Ls1, Ds1);
-        }
+    // Every tile's synchronisation happens once, before it: here for the
+    // first, at the end of stage C of the one before for the others.
+    if (total > 0) {
+        load(std::integral_constant<int, 0>{}, 0);
+        sync(std::integral_constant<int, 1>{}, 0);
+        read_block0(std::integral_constant<int, 0>{});
+    }
+    for (int hh = 0; hh < G && nqt > 0; ++hh) {
+        const int base = hh * nqt - qt_lo;
+        // tiles [a, b) in pairs, so that each tile's stage is named at compile time
+        auto run = [&](auto MASK, int a, int b) __attribute__((always_inline)) {
+            constexpr std::integral_constant<int, 0> S0{};
+            constexpr std::integral_constant<int, 1> S1{};
+            int qt = a;
+            if (qt < b && ((base + qt) & 1)) {
+                tile(MASK, S1, base + qt, qt);
+                ++qt;
+            }
+            for (; qt + 1 < b; qt += 2) {
+                tile(MASK, S0, base + qt, qt);
+                tile(MASK, S1, base + qt + 1, qt + 1);
+            }
+            if (qt < b) tile(MASK, S0, base + qt, qt);
+        };
+        run(std::true_type{}, qt_lo, m1);
+        run(std::false_type{}, m1, m2);
+        run(std::true_type{}, m2, qt_end);
     }
 
     if (my_k < Nk) {
