@@ -335,10 +335,19 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_fp8_kernel(FwdParams p)
     lds_wait_vm();
     __syncthreads();
     const int nphase = 2 * n + 2;
-    // Block-scale codes of the tiles, loaded with the tiles themselves and
-    // kept per stage like them: sk0/sk1 for K_j (j even/odd), sv0/sv1 for V_j.
+    // Block-scale codes of the tiles, kept per stage like the tiles: sk0/sk1
+    // for K_j (j even/odd), sv0/sv1 for V_j.  Each is read by a scalar load of
+    // the aligned dword that holds it (that dword lies within the array's own
+    // page): a vector load would share its wait counter with the tile loads
+    // issued beside it, so that waiting for the code would wait for the tiles.
+    typedef __attribute__((address_space(4))) const int const_int_t;
+    auto code_at = [&](const int8_t *e, int j) __attribute__((always_inline)) -> int {
+        const uintptr_t a = (uintptr_t)(e + j);
+        const int w = *(const_int_t *)(a & ~(uintptr_t)3);
+        return 127 + (int)(int8_t)(w >> (8 * (int)(a & 3)));
+    };
     int sk0 = 127, sk1 = 127, sv0 = 127, sv1 = 127;
-    if (BLK && n > 0) sk0 = 127 + kexp[0];
+    if (BLK && n > 0) sk0 = code_at(kexp, 0);
     // G: the wavefront's group; P: the parity of global phase t (both
     // compile-time, so that each group's loop is straight-line code).
     auto phase = [&](auto G, auto P, int t, const uint8_t *kcur, const uint8_t *vprev, uint8_t *knext,
@@ -348,8 +357,8 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_fp8_kernel(FwdParams p)
         if constexpr (par == 0) {
             if (BLK) {
                 const int j = t >> 1;
-                if (j + 1 < n) skn = 127 + kexp[j + 1];
-                if (j < n) svn = 127 + vexp[j];
+                if (j + 1 < n) skn = code_at(kexp, j + 1);
+                if (j < n) svn = code_at(vexp, j);
             }
         }
         constexpr bool MSTEP = ((par - g) & 1) == 0;
