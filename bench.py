@@ -89,10 +89,8 @@ def kernel_source_hash(names) -> str:
 def traffic_file(w, bwd: bool):
     """The committed counter summary for this workload, if one is kept."""
     from exact_attention_93_amd import workloads as W
-    if bwd:
-        return None
-    if w.name == W.HEADLINE:
-        return os.path.join(PROFILES, "fa_fwd_bf16_causal_B2_H32_N4096_d128_traffic.txt")
+    if bwd:   # both kernels of the step (dq, then dk/dv)
+        return os.path.join(PROFILES, f"fa_bwd_bf16_{w.name}_traffic.txt")
     if w.name.startswith("decode_"):
         return os.path.join(PROFILES, f"fa_decode_bf16_{w.name}_traffic.txt")
     kern = {"fp8": "fwd_fp8", "fp8blk": "fwd_fp8", "fp32": "fwd_f32"}.get(w.dtype, "fwd_bf16")
