@@ -165,7 +165,7 @@ def test_rotation_reduces_the_error_of_outlier_features():
 
 
 def test_rotation_error_report_other_outliers():
-    """Two further regimes, reported (not asserted; the design doc records them):
+    """Two further regimes, reported in the test output, not asserted:
     rare large outliers (the rotation helps a little) and outlier channels
     that differ between q and k (it can hurt: spreading both over all
     coordinates enlarges the sum of squared products that the rounding
