@@ -292,11 +292,13 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p)
     };
 
     // One 32-key half of the tile at a time: S^T and dP^T for those keys,
-    // dS^T in bf16, then its share of dQ^T += K^T dS^T.
-    auto compute = [&](int j, const uint16_t *ks_, const uint16_t *vs_) {
+    // dS^T in bf16, then its share of dQ^T += K^T dS^T.  With MASK (tiles
+    // that cross the diagonal or the end of the keys), keys past the row's
+    // last visible one get P = 0; the other tiles skip the test.
+    auto compute = [&](auto MASK, int j, const uint16_t *ks_, const uint16_t *vs_) __attribute__((always_inline)) {
+        constexpr bool need_mask = decltype(MASK)::value;
         const char *ks = (const char *)ks_, *vs = (const char *)vs_;
         const int key0 = j * BN;
-        const bool need_mask = (key0 + BN > Nk) || (CAUSAL && key0 + BN - 1 > wq0 + off);
         const int lim = (CAUSAL ? min(my_q + off, Nk - 1) : Nk - 1) - (key0 + 8 * hf);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -319,7 +321,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p)
                     for (int z = 0; z < 2; ++z) {
                         const int i = 8 * u + 2 * w + z;
                         float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lse2));
-                        if (need_mask && kb * 32 + 16 * u + 2 * w + z > lim) pv = 0.f;
+                        if constexpr (need_mask) pv = (kb * 32 + 16 * u + 2 * w + z > lim) ? 0.f : pv;
                         e2[z] = pv * (dp[i] - delta);
                     }
                     dsb[u][w] = pack_bf16(e2[0], e2[1]);
@@ -332,17 +334,23 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p)
         }
     };
 
+    auto step = [&](int j, const uint16_t *ks_, const uint16_t *vs_) __attribute__((always_inline)) {
+        if (!visible(j)) return;
+        const int key0 = j * BN;
+        if ((key0 + BN > Nk) || (CAUSAL && key0 + BN - 1 > wq0 + off)) compute(std::true_type{}, j, ks_, vs_);
+        else compute(std::false_type{}, j, ks_, vs_);
+    };
     if (n > 0) load(0, Ks0, Vs0);
     for (int j = 0; j < n; j += 2) {
         vm_wait_all();
         __syncthreads();                  // tile j resident; every wavefront is done with tile j-1
         if (j + 1 < n) load(j + 1, Ks1, Vs1);
-        if (visible(j)) compute(j, Ks0, Vs0);
+        step(j, Ks0, Vs0);
         if (j + 1 < n) {
             vm_wait_all();
             __syncthreads();
             if (j + 2 < n) load(j + 2, Ks0, Vs0);
-            if (visible(j + 1)) compute(j + 1, Ks1, Vs1);
+            step(j + 1, Ks1, Vs1);
         }
     }
 
