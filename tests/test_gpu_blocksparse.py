@@ -78,4 +78,4 @@ def test_blocksparse_butterfly_workload():
     say(f"case workload {w.name}")
     q, k, v = W.gen_inputs(w)
     mask = W.butterfly_mask(w.Hq, w.N)
-    check(q, k, v, mask, w.causal, w.scale, w.name, rows=W.sample_rows(w, per_head=128), exact_bounds=True)
+    check(q, k, v, mask, w.causal, w.scale, w.name, rows=W.sample_rows(w, per_head=512), exact_bounds=True)
