@@ -375,7 +375,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p)
 // Each query tile (two 32-row blocks) runs as four stages, each a run of
 // products with other work placed between them:
 //   A: S0, dP0            | row operands of block 1, lse/delta of block 0
-//   B: S1, dP1            | softmax of block 0, transposed operands of block 0
+//   B: S1, dP1            | softmax of block 0, its transposed operands, lse/delta of block 1
 //   C: dV += dO0^T P0 ... | softmax of block 1, transposed operands of block 1
 //   D: dV, dK of block 1  | row operands of block 0 of the next tile
 // The tile's synchronisation (its data resident, the previous buffer free)
