@@ -414,4 +414,6 @@ const char *fa_strerror(int status)
 
 int fa_version(void) { return kVersion; }
 
+int fa_fwd_lds_stages(void) { return fa::fwd_bf16_lds_stages(); }
+
 }  // extern "C"

@@ -211,6 +211,16 @@ __device__ __forceinline__ void lds_wait_vm()
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Debug build (FA_SINGLE_STAGE=1): one K stage and one V stage.  A tile is
+// loaded only after the barrier that ends every read of the stage, and read
+// only after its loads have completed and a barrier, so the double-buffered
+// schedule's only changes are where the loads are issued and which stage
+// they fill; its output must equal the double-buffered build's bit for bit.
+#ifndef FA_SINGLE_STAGE
+#define FA_SINGLE_STAGE 0
+#endif
+constexpr bool kSingleStage = FA_SINGLE_STAGE != 0;
+
 // Block-sparse forward: query blocks of kMaskRows rows x key tiles of kBN
 // keys; the workgroup visits only the tiles that one of its query blocks keeps.
 constexpr int kMaskRows = 128;
@@ -732,12 +742,12 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
         // Even phases load K_{j+1} and V_j (j = t/2): with a block mask at the
         // start of the phase, otherwise spread through the leading group's
         // products.
-        if constexpr (!SPREAD && par == 0) {
+        if constexpr (!SPREAD && !kSingleStage && par == 0) {
             const int j = t >> 1;
             if (j + 1 < n) load_k(j + 1, knext);
             if (j < n) load_v(j, vnext);
         }
-        constexpr bool LD = SPREAD && par == 0 && g == 0;
+        constexpr bool LD = SPREAD && !kSingleStage && par == 0 && g == 0;
         constexpr bool MSTEP = ((par - g) & 1) == 0;   // local step s = t - g is even
         const int s = t - g;
         if (s >= 0 && s <= 2 * n) {
@@ -765,6 +775,22 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
         }
     };
     auto run = [&](auto G) __attribute__((always_inline)) {
+        if constexpr (kSingleStage) {
+            for (int t = 0; t < nphase; t += 2) {
+                // The barrier after phase t - 1 ended every read of the stage
+                // (K_0 was loaded before the loop).
+                const int j = t >> 1;
+                if (j >= 1) {
+                    if (j < n) load_k(j, Ks0);
+                    if (j - 1 < n) load_v(j - 1, Vs0);
+                    lds_wait_vm();
+                    __syncthreads();
+                }
+                phase(G, ic<0>(), t, Ks0, Vs0, Ks1, Vs1);
+                phase(G, ic<1>(), t + 1, Ks0, Vs0, Ks1, Vs1);
+            }
+            return;
+        }
         for (int t = 0; t < nphase; t += 4) {
             // even j = t/2: K_j in Ks0, V_{j-1} in Vs1; loads go to Ks1, Vs0
             phase(G, ic<0>(), t, Ks0, Vs1, Ks1, Vs0);
@@ -843,6 +869,8 @@ hipError_t launch_d(const FwdParams &p, hipStream_t stream)
 }
 
 }  // namespace
+
+int fwd_bf16_lds_stages() { return kSingleStage ? 1 : 2; }
 
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, hipStream_t stream)
 {

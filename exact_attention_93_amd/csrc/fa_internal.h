@@ -43,6 +43,7 @@ struct FwdParams {
 };
 
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, hipStream_t stream);
+int fwd_bf16_lds_stages();   // 1 in the single-stage debug build, else 2
 hipError_t launch_fwd_fp8(const FwdParams &p, int d, hipStream_t stream);
 // Few query rows per K/V head (decoding): rows of one head group packed into
 // 32-row blocks, K/V read once per group.
