@@ -31,7 +31,7 @@ from ._build import LIB_PATH, SINGLE_STAGE_LIB_PATH
 
 __all__ = ["fwd", "fa_fwd_splitkv_static", "fwd_blocksparse", "fa_fwd_blocksparse", "fwd_fp8", "fa_fwd_fp8", "fwd_fp8_block",
            "fa_fwd_fp8_block", "quantize_fp8", "fa_quantize_fp8", "bwd", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_splitkv_num_splits",
-           "fa_splitkv_workspace_size", "fa_strerror", "fa_version", "fa_fwd_lds_stages", "load_library", "FAError",
+           "fa_splitkv_workspace_size", "fa_strerror", "fa_version", "fa_lds_stages", "load_library", "FAError",
            "STATUS", "EXPORTS"]
 
 STATUS = {
@@ -43,7 +43,7 @@ STATIC_SCRATCH_BYTES = 32 << 20   # FA_STATIC_SCRATCH_BYTES
 EXPORTS = ("fa_fwd", "fa_fwd_f32", "fa_fwd_splitkv", "fa_fwd_splitkv_f32", "fa_fwd_splitkv_static",
            "fa_splitkv_num_splits",
            "fa_splitkv_workspace_size", "fa_fwd_blocksparse", "fa_fwd_fp8", "fa_fwd_fp8_block", "fa_quantize_fp8",
-           "fa_bwd", "fa_bwd_workspace_size", "fa_strerror", "fa_version", "fa_fwd_lds_stages")
+           "fa_bwd", "fa_bwd_workspace_size", "fa_strerror", "fa_version", "fa_lds_stages")
 
 _lib = None
 
@@ -102,8 +102,8 @@ def load_library(path: str = LIB_PATH):
     lib.fa_strerror.argtypes = [ctypes.c_int]
     lib.fa_version.restype = ctypes.c_int
     lib.fa_version.argtypes = []
-    lib.fa_fwd_lds_stages.restype = ctypes.c_int
-    lib.fa_fwd_lds_stages.argtypes = []
+    lib.fa_lds_stages.restype = ctypes.c_int
+    lib.fa_lds_stages.argtypes = []
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -139,8 +139,8 @@ def fa_version() -> int:
     return load_library().fa_version()
 
 
-def fa_fwd_lds_stages() -> int:
-    return load_library().fa_fwd_lds_stages()
+def fa_lds_stages() -> int:
+    return load_library().fa_lds_stages()
 
 
 def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, scale, causal, stream) -> int:

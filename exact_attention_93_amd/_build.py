@@ -1,9 +1,10 @@
 """Compile the HIP sources into the in-tree shared libraries (gfx950):
 
 libfa.so               the library;
-libfa_single_stage.so  the same library with its bf16 forward kernels built
-                       with one K/V LDS stage (FA_SINGLE_STAGE=1), a debug
-                       build whose outputs must equal libfa.so's bit for bit.
+libfa_single_stage.so  the same library with its forward and backward kernels
+                       built with one LDS stage per streamed tile
+                       (FA_SINGLE_STAGE=1), a debug build whose outputs must
+                       equal libfa.so's bit for bit.
 
 Every source is compiled to an object in a temporary directory (in
 parallel), and each library is linked from those objects."""
@@ -21,7 +22,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libfa.so")
 SINGLE_STAGE_LIB_PATH = os.path.join(PKG, "libfa_single_stage.so")
-SINGLE_STAGE_SOURCES = ("fa_fwd_bf16.hip",)   # the sources that read FA_SINGLE_STAGE
+SINGLE_STAGE_SOURCES = ("fa_fwd_bf16.hip", "fa_fwd_fp8.hip", "fa_bwd_bf16.hip")   # read FA_SINGLE_STAGE
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are switched off for all device code.

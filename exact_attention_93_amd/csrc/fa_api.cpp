@@ -414,6 +414,10 @@ const char *fa_strerror(int status)
 
 int fa_version(void) { return kVersion; }
 
-int fa_fwd_lds_stages(void) { return fa::fwd_bf16_lds_stages(); }
+int fa_lds_stages(void)
+{
+    const int n = fa::fwd_bf16_lds_stages();
+    return (n == fa::fwd_fp8_lds_stages() && n == fa::bwd_lds_stages()) ? n : 0;
+}
 
 }  // extern "C"

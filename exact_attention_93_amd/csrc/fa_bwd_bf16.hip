@@ -341,6 +341,17 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdParams p)
         else compute(std::false_type{}, j, ks_, vs_);
     };
     if (n > 0) load(0, Ks0, Vs0);
+    if constexpr (kSingleStage) {
+        for (int j = 0; j < n; ++j) {
+            if (j > 0) {
+                __syncthreads();          // every wavefront is done with tile j-1
+                load(j, Ks0, Vs0);
+            }
+            vm_wait_all();
+            __syncthreads();              // tile j resident
+            step(j, Ks0, Vs0);
+        }
+    } else
     for (int j = 0; j < n; j += 2) {
         vm_wait_all();
         __syncthreads();                  // tile j resident; every wavefront is done with tile j-1
@@ -397,7 +408,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p)
     // its own with no branch around the load
     __shared__ __attribute__((aligned(16))) char Ls0[4 * BQ * 4], Ls1[4 * BQ * 4], Ds0[4 * BQ * 4], Ds1[4 * BQ * 4];
     auto stage = [&](auto S) __attribute__((always_inline)) {
-        if constexpr (decltype(S)::value == 0) return std::make_tuple(Qs0, Os0, Ls0, Ds0);
+        if constexpr (decltype(S)::value == 0 || kSingleStage) return std::make_tuple(Qs0, Os0, Ls0, Ds0);
         else return std::make_tuple(Qs1, Os1, Ls1, Ds1);
     };
 
@@ -510,6 +521,15 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p)
         vm_wait_all();
         __syncthreads();
         load(S, it + 1);
+    };
+    // The single-stage build's synchronisation before tile it: every
+    // wavefront done with tile it-1, then tile it loaded into the one stage
+    // and resident.
+    auto sync_single = [&](int it) __attribute__((always_inline)) {
+        __syncthreads();
+        load(std::integral_constant<int, 0>{}, it);
+        vm_wait_all();
+        __syncthreads();
     };
 
     f32x16_t dk[XB], dv[XB];
@@ -674,7 +694,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p)
         // keep block 1's softmax here, ahead of the synchronisation below
         asm volatile("" : "+v"(pb1[0]), "+v"(pb1[1]), "+v"(dsb1[0]), "+v"(dsb1[1]));
         // ---- the next tile's synchronisation; then D: dV, dK of block 1 | row operands of block 0 of tile it+1
-        sync(S, it + 1);          // tile it+2 goes into this tile's stage
+        if constexpr (kSingleStage) sync_single(it + 1);
+        else sync(S, it + 1);     // tile it+2 goes into this tile's stage
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -693,8 +714,12 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams p)
     // Every tile's synchronisation happens once, before it: here for the
     // first, at the end of stage C of the one before for the others.
     if (total > 0) {
-        load(std::integral_constant<int, 0>{}, 0);
-        sync(std::integral_constant<int, 1>{}, 0);
+        if constexpr (kSingleStage) {
+            sync_single(0);
+        } else {
+            load(std::integral_constant<int, 0>{}, 0);
+            sync(std::integral_constant<int, 1>{}, 0);
+        }
         read_block0(std::integral_constant<int, 0>{});
     }
     for (int hh = 0; hh < G && nqt > 0; ++hh) {
@@ -752,6 +777,8 @@ hipError_t launch_one(const BwdParams &p, hipStream_t stream)
 }
 
 }  // namespace
+
+int bwd_lds_stages() { return kSingleStage ? 1 : 2; }
 
 hipError_t launch_bwd_bf16(const BwdParams &p, int d, hipStream_t stream)
 {

@@ -211,16 +211,6 @@ __device__ __forceinline__ void lds_wait_vm()
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// Debug build (FA_SINGLE_STAGE=1): one K stage and one V stage.  A tile is
-// loaded only after the barrier that ends every read of the stage, and read
-// only after its loads have completed and a barrier, so the double-buffered
-// schedule's only changes are where the loads are issued and which stage
-// they fill; its output must equal the double-buffered build's bit for bit.
-#ifndef FA_SINGLE_STAGE
-#define FA_SINGLE_STAGE 0
-#endif
-constexpr bool kSingleStage = FA_SINGLE_STAGE != 0;
-
 // Block-sparse forward: query blocks of kMaskRows rows x key tiles of kBN
 // keys; the workgroup visits only the tiles that one of its query blocks keeps.
 constexpr int kMaskRows = 128;

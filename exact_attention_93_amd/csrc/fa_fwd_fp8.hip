@@ -203,6 +203,10 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_fp8_kernel(FwdParams p)
         const uint32_t off = (uint32_t)(j * kBN + ld_row) * (uint32_t)sK + ((ld_pch ^ k_swz(ld_row)) * 16);
         load_lds16(kbase, range, off, (lds_void_t *)&dst[wave * 1024]);
     };
+    auto load_v = [&](int j, uint8_t *dst) {   // the single-stage build's V loads
+        const uint32_t off = (uint32_t)(j * kBN + ld_row) * (uint32_t)sK + ((ld_pch ^ v_swz(ld_row)) * 16);
+        load_lds16(vbase, range, off, (lds_void_t *)&dst[wave * 1024]);
+    };
     // Tile loads of an even phase: the leading group's four wavefronts move
     // two 1 KB blocks of K_{j+1} and two of V_j each at the start of their
     // matrix-core step (with all eight wavefronts loading one block each at
@@ -353,8 +357,8 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_fp8_kernel(FwdParams p)
     auto phase = [&](auto G, auto P, int t, const uint8_t *kcur, const uint8_t *vprev, uint8_t *knext,
                      uint8_t *vnext, const int &skc, const int &svp, int &skn, int &svn) __attribute__((always_inline)) {
         constexpr int g = decltype(G)::value, par = decltype(P)::value;
-        if constexpr (par == 0 && g == 0) issue_kv(t >> 1, knext, vnext);
-        if constexpr (par == 0) {
+        if constexpr (par == 0 && g == 0 && !kSingleStage) issue_kv(t >> 1, knext, vnext);
+        if constexpr (par == 0 && !kSingleStage) {
             if (BLK) {
                 const int j = t >> 1;
                 if (j + 1 < n) skn = code_at(kexp, j + 1);
@@ -380,6 +384,26 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_fp8_kernel(FwdParams p)
         }
     };
     auto run = [&](auto G) __attribute__((always_inline)) {
+        if constexpr (kSingleStage) {
+            for (int t = 0; t < nphase; t += 2) {
+                // The barrier after phase t - 1 ended every read of the stage
+                // (K_0 and its code were loaded before the loop).
+                const int j = t >> 1;
+                if (j >= 1) {
+                    if (j < n) load_k(j, Ks0);
+                    load_v(j - 1, Vs0);
+                    if (BLK) {
+                        if (j < n) sk0 = code_at(kexp, j);
+                        sv0 = code_at(vexp, j - 1);
+                    }
+                    lds_wait_vm();
+                    __syncthreads();
+                }
+                phase(G, ic<0>(), t, Ks0, Vs0, Ks1, Vs1, sk0, sv0, sk1, sv1);
+                phase(G, ic<1>(), t + 1, Ks0, Vs0, Ks1, Vs1, sk0, sv0, sk1, sv1);
+            }
+            return;
+        }
         for (int t = 0; t < nphase; t += 4) {
             phase(G, ic<0>(), t, Ks0, Vs1, Ks1, Vs0, sk0, sv1, sk1, sv0);
             phase(G, ic<1>(), t + 1, Ks0, Vs1, Ks1, Vs0, sk0, sv1, sk1, sv0);
@@ -421,6 +445,8 @@ hipError_t launch_one(const FwdParams &p, hipStream_t stream)
 }
 
 }  // namespace
+
+int fwd_fp8_lds_stages() { return kSingleStage ? 1 : 2; }
 
 hipError_t launch_fwd_fp8(const FwdParams &p_in, int d, hipStream_t stream)
 {

@@ -42,8 +42,23 @@ struct FwdParams {
     int mask_nqb, mask_nkb;
 };
 
+// Debug build switch (FA_SINGLE_STAGE=1): the bf16 and fp8 forward kernels
+// keep one K/V LDS stage and the backward kernels one K/V (dQ) and one Q/dO
+// (dK/dV) stage.  A tile is loaded only after the barrier that ends every
+// read of the stage, and read only after its loads have completed and a
+// barrier: no load overlaps a read.  The arithmetic and its order are those
+// of the normal (double-buffered) build, so the outputs must be equal bit
+// for bit; a difference points at a missing wait or barrier.
+#ifndef FA_SINGLE_STAGE
+#define FA_SINGLE_STAGE 0
+#endif
+constexpr bool kSingleStage = FA_SINGLE_STAGE != 0;
+// the stage count each kernel source was built with (1 or 2)
+int fwd_bf16_lds_stages();
+int fwd_fp8_lds_stages();
+int bwd_lds_stages();
+
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, hipStream_t stream);
-int fwd_bf16_lds_stages();   // 1 in the single-stage debug build, else 2
 hipError_t launch_fwd_fp8(const FwdParams &p, int d, hipStream_t stream);
 // Few query rows per K/V head (decoding): rows of one head group packed into
 // 32-row blocks, K/V read once per group.

@@ -294,15 +294,16 @@ const char *fa_strerror(int status);
 /* Library version as major*10000 + minor*100 + patch. */
 int fa_version(void);
 
-/* K/V LDS stages of the bf16 forward kernels this library was built with
- * (the forward of fa_fwd, fa_fwd_splitkv, fa_fwd_splitkv_static and
- * fa_fwd_blocksparse): 2 in the normal build, where the next tile streams
- * into one stage while the other is read, and 1 in the debug build
- * (libfa_single_stage.so), which loads each tile only after every read of
- * the one stage has ended.  The debug build exists to check the
- * double-buffered build's barrier placement: its outputs must be equal bit
- * for bit.  No error case. */
-int fa_fwd_lds_stages(void);
+/* LDS stages of the kernels this library was built with: 2 in the normal
+ * build, where the next tile (K/V in the forward kernels and the dQ kernel,
+ * Q/dO in the dK/dV kernel) streams into one stage while the other is read;
+ * 1 in the debug build (libfa_single_stage.so), which loads each tile only
+ * after every read of the one stage has ended; 0 if the kernel sources were
+ * built inconsistently.  The debug build exists to check the normal build's
+ * wait and barrier placement: its outputs must be equal bit for bit.  Covers
+ * the bf16 and fp8 forward kernels and the backward; the fp32 forward and
+ * the decoding kernel keep one stage in both builds.  No error case. */
+int fa_lds_stages(void);
 
 #ifdef __cplusplus
 }
