@@ -32,8 +32,10 @@
 //    values down to 2^-17 of the maximum keep a code.
 //  * The sum of the quantised probabilities, which normalises O (so that O
 //    stays a convex combination of the V rows), comes from the matrix cores:
-//    a fifth product per tile with an all-ones A operand.  The fp32 sum of
-//    the unquantised values gives the log-sum-exp.
+//    one 16x16x128 product per tile whose B operand is the P'^T register set
+//    of the P V products and whose A operand is a 0/1 selector (below).  The
+//    sum of e4m3 values is exact in fp32 in any order.  The fp32 sum of the
+//    unquantised values gives the log-sum-exp.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -45,6 +47,7 @@ namespace {
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -73,6 +76,11 @@ __device__ __forceinline__ f32x16_t mfma_fp8(i32x8_t a, i32x8_t b, f32x16_t c)
 __device__ __forceinline__ f32x16_t mfma_fp8_scaled(i32x8_t a, i32x8_t b, f32x16_t c, int sa, int sb)
 {
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+__device__ __forceinline__ f32x4_t mfma16_fp8(i32x8_t a, i32x8_t b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
@@ -236,39 +244,31 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_fp8_kernel(FwdParams p)
     const int tr_row = 8 * (tg >> 1) + (ts >> 1);   // + 16 jb
     const int tr_chunk = tg & 1;                    // + 2 xb
     const int tr_byte = 8 * (ts & 1);
-    const i32x8_t ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                          0x38383838, 0x38383838, 0x38383838, 0x38383838};   // e4m3 1.0
+    // Row-sum selector.  Read as the B operand of a 16x16x128 product, lane
+    // l's P'^T bytes are 32 keys of query l % 32, i.e. query n + 16 (g % 2)
+    // for column n = l % 16 and K group g = l / 16.  The A operand holds e4m3
+    // 1.0 where the K group's parity equals that of the output row block
+    // (rows 4r .. 4r+3, r = row / 4) and 0 elsewhere, so every accumulator
+    // register of lane l receives the sum over all 64 keys of its own query
+    // l % 32.
+    const int sel_w = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1) ? 0x38383838 : 0;
+    const i32x8_t sum_sel = {sel_w, sel_w, sel_w, sel_w, sel_w, sel_w, sel_w, sel_w};
 
     float m_run = -INFINITY;   // running maximum (base 2), shared by both halves
     float l_run = 0.f;         // fp32 sum of this half's unquantised probabilities
-    f32x16_t oacc[XB], lacc;   // O^T, and the sum of the quantised probabilities
+    f32x16_t oacc[XB];         // O^T
+    f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};   // the sum of the quantised probabilities
 #pragma unroll
     for (int xb = 0; xb < XB; ++xb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[xb][i] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) lacc[i] = 0.f;
     f32x16_t sacc[NKB];
     i32x8_t pb;                // P'^T (e4m3) of the tile whose product is next
 
+    // Matrix-core step for tile j: S_j^T = K_j Q^T first (the next softmax
+    // step reads it at once), then O^T += V_{j-1}^T P_{j-1}^T and the sum of
+    // the quantised probabilities.
     auto mfma_step = [&](int j, const uint8_t *kcur, const uint8_t *vprev, int sk, int sv) __attribute__((always_inline)) {
-        if (j >= 1 && visible(j - 1)) {
-            const char *vs = (const char *)vprev;
-#pragma unroll
-            for (int xb = 0; xb < XB; ++xb) {
-                i32x8_t a;
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) {
-                    const int row = 16 * jb + tr_row;
-                    const int off = row * ROW_BYTES + (((2 * xb + tr_chunk) ^ v_swz(row)) * 16) + tr_byte;
-                    const i32x2_t t2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t *)(vs + off));
-                    a[2 * jb] = t2[0];
-                    a[2 * jb + 1] = t2[1];
-                }
-                oacc[xb] = BLK ? mfma_fp8_scaled(a, pb, oacc[xb], sv, 127) : mfma_fp8(a, pb, oacc[xb]);
-            }
-            lacc = mfma_fp8(ones, pb, lacc);
-        }
         if (j < n && visible(j)) {
             const char *ks = (const char *)kcur;
 #pragma unroll
@@ -287,6 +287,23 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_fp8_kernel(FwdParams p)
                     sacc[kb] = BLK ? mfma_fp8_scaled(a, qreg[t], sacc[kb], sk, sq) : mfma_fp8(a, qreg[t], sacc[kb]);
                 }
             }
+        }
+        if (j >= 1 && visible(j - 1)) {
+            const char *vs = (const char *)vprev;
+#pragma unroll
+            for (int xb = 0; xb < XB; ++xb) {
+                i32x8_t a;
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) {
+                    const int row = 16 * jb + tr_row;
+                    const int off = row * ROW_BYTES + (((2 * xb + tr_chunk) ^ v_swz(row)) * 16) + tr_byte;
+                    const i32x2_t t2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t *)(vs + off));
+                    a[2 * jb] = t2[0];
+                    a[2 * jb + 1] = t2[1];
+                }
+                oacc[xb] = BLK ? mfma_fp8_scaled(a, pb, oacc[xb], sv, 127) : mfma_fp8(a, pb, oacc[xb]);
+            }
+            lacc = mfma16_fp8(sum_sel, pb, lacc);
         }
     };
 
