@@ -74,12 +74,12 @@ def test_bwd_deterministic():
 
 def test_bwd_headline_workload_sampled():
     """The causal B=2 H=32 N=4096 d=128 workload, launched as the benchmark
-    launches it; the oracle checks four whole head groups (every dq, dk, dv
-    element of those heads)."""
+    launches it; four whole head groups are checked (every dq, dk, dv element
+    of those heads, whose o and lse come from the oracle)."""
     w = W.WORKLOADS[W.HEADLINE]
     q, k, v = W.gen_inputs(w)
     g = torch.Generator().manual_seed(w.seed + 50)
     do = torch.randn(q.shape, generator=g).to(torch.bfloat16)
-    grads = gpu_fwd_bwd(q, k, v, do, w.causal, w.scale)
-    compare_bwd(q, k, v, do, w.causal, w.scale, *grads, groups=[(0, 0), (0, 17), (1, 5), (1, 31)],
-                label=w.name)
+    groups = [(0, 0), (0, 17), (1, 5), (1, 31)]
+    grads = gpu_fwd_bwd(q, k, v, do, w.causal, w.scale, groups=groups)
+    compare_bwd(q, k, v, do, w.causal, w.scale, *grads, groups=groups, label=w.name)
