@@ -50,6 +50,7 @@ METRIC = "attn fwd TFLOP/s at N=4096,d=128 causal bf16; % of dense bf16 MFMA pea
 # fp8, written out exactly: 256 CUs x 2048 bf16 FMA per clock x 2 x 2.4 GHz).
 PEAK_BF16_TFLOPS = 2516.6
 PEAK_FP8_TFLOPS = 5033.2
+PEAK_FP32_TFLOPS = 157.3        # dense fp32 matrix-core peak (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E peak bandwidth (published)
 # Untimed back-to-back steps run for at least this long before the timed
 # region, whatever --warmup asks for: the GPU's clock needs tens of
@@ -269,7 +270,9 @@ def main():
         raise SystemExit(f"bench.py: invalid split arguments for {w.name}")
     ws_bytes = fa.fa_splitkv_workspace_size(w.B, w.Hq, w.Hkv, w.N, w.Nkv, w.d, w.splits)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev) if ws_bytes else None
-    hbm_bound = w.flops / w.io_bytes < PEAK_BF16_TFLOPS / PEAK_HBM_GBS * 1e3
+    fp32 = w.dtype == "fp32"
+    peak_mfma = PEAK_FP8_TFLOPS if fp8 else PEAK_FP32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
+    hbm_bound = w.flops / w.io_bytes < peak_mfma / PEAK_HBM_GBS * 1e3
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib * (1 << 20) // 4
@@ -400,7 +403,7 @@ def main():
     if hbm_bound:
         unit, peak, work = "GB/s", PEAK_HBM_GBS, w.io_bytes / 1e9
     else:
-        unit, peak, work = "TFLOP/s", PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS, flops / 1e12
+        unit, peak, work = "TFLOP/s", peak_mfma, flops / 1e12
     value = work / (ms_per_step * 1e-3)
     achieved = work / (mean_launch_ms * 1e-3)
     headline = w.name == W.HEADLINE and not bwd
@@ -416,6 +419,9 @@ def main():
     elif sparse:
         metric = (f"attn fwd TFLOP/s on {w.name} (FLOPs of the kept blocks only); "
                   "% of dense bf16 MFMA peak")
+    elif fp32:
+        metric = f"attn fwd {unit} on {w.name} (fp32 in and out)" + (
+            "; % of HBM peak" if hbm_bound else "; % of dense fp32 MFMA peak")
     else:
         metric = METRIC if headline else (
             f"attn fwd {unit} on {w.name}" + ("; % of HBM peak" if hbm_bound else "; % of dense bf16 MFMA peak"))
@@ -451,7 +457,9 @@ def main():
     }
     if w.Nkv != w.N or splits > 1:
         out["config"].update({"Nk": w.Nkv, "splits": splits, "algorithmic_bytes_per_step": w.io_bytes})
-        out["dtype"] = "bf16" if w.dtype == "bf16" else "f32"
+    if fp32:
+        out["dtype"] = "f32"
+        out["data"] = "synthetic (seeded randn, fp32)"
     if bwd:
         out["config"]["pass"] = "bwd"
     if sparse:

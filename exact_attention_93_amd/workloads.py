@@ -131,7 +131,17 @@ SPARSE_WORKLOADS = {
     "butterfly_bf16_B1_H32_N16384_d128": Workload(
         "butterfly_bf16_B1_H32_N16384_d128", 1, 32, 32, 16384, 128, "bf16", False, 1.0, 1010, mask="butterfly"),
 }
-ALL_WORKLOADS = {**WORKLOADS, **SPLIT_WORKLOADS, **FP8_WORKLOADS, **D256_WORKLOADS, **SPARSE_WORKLOADS}
+# fp32 inputs and outputs at scale (the accuracy path): the headline shape,
+# and a split call of 256 new queries against a 64K-key context.
+FP32_WORKLOADS = {
+    "causal_fp32_B2_H32_N4096_d128": Workload(
+        "causal_fp32_B2_H32_N4096_d128", 2, 32, 32, 4096, 128, "fp32", True, 1.0, 1012),
+    "chunk_causal_fp32_B1_H8_Nq256_Nk65536_d128": Workload(
+        "chunk_causal_fp32_B1_H8_Nq256_Nk65536_d128", 1, 8, 8, 256, 128, "fp32", True, 1.0, 1013,
+        Nk=65536, splits=0),
+}
+ALL_WORKLOADS = {**WORKLOADS, **SPLIT_WORKLOADS, **FP8_WORKLOADS, **D256_WORKLOADS, **SPARSE_WORKLOADS,
+                 **FP32_WORKLOADS}
 MASK_BLOCK = (128, 64)      # query rows x keys per block-mask entry of the GPU library
 
 
