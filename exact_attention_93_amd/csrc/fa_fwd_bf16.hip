@@ -501,6 +501,73 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
         }
     };
 
+    // d = 256: the products are inline assembly (O^T in AGPRs), which the
+    // scheduling-group masks do not match, so their operand reads are placed
+    // explicitly: a ring of operands read RING products ahead, and a
+    // scheduling barrier after each product, so that no read slides back to
+    // its product and leaves the only wavefront of the SIMD waiting on it.
+    // Product order: P V by (u, xb) with xb inner; scores by (t, kb) with kb
+    // inner, so that consecutive score products feed different accumulators.
+    constexpr int RING = 4;
+    auto vt_operand = [&](const char *vs, int i) __attribute__((always_inline)) -> u32x4_t {
+        const int u = i / XB, xb = i % XB;
+        u32x4_t a;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int row = 16 * u + 4 * r + tr_row;
+            const int off = row * ROW_BYTES + (((4 * xb + tr_chunk) ^ v_swz<D>(row)) * 16) + tr_byte;
+            const i16x4_t t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(vs + off));
+            const u32x2_t t2 = __builtin_bit_cast(u32x2_t, t4);
+            a[2 * r] = t2[0];
+            a[2 * r + 1] = t2[1];
+        }
+        return a;
+    };
+    auto k_operand = [&](const char *ks, int i) __attribute__((always_inline)) -> u32x4_t {
+        const int t = i / NKB, kb = i % NKB;
+        const int row = kb * 32 + krow;
+        return *(const u32x4_t *)(ks + row * ROW_BYTES + (((2 * t + hf) ^ k_swz<D>(row)) * 16));
+    };
+    auto pv_ring = [&](const char *vs) __attribute__((always_inline)) {
+        constexpr int NP = PVSTEPS * XB;
+        u32x4_t ring[RING];
+#pragma unroll
+        for (int i = 0; i < RING; ++i) ring[i] = vt_operand(vs, i);
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            mma_o_a(oacc[i % XB], ring[i % RING], pb[i / XB]);
+            if (i + RING < NP) ring[i % RING] = vt_operand(vs, i + RING);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    // The scores, with the phase's tile loads (LD: K_{jl+1} and V_{jl}, one
+    // 1 KB block of each per two products from the start).
+    auto s_ring = [&](const char *ks, auto LOADS, int jl, uint16_t *knext, uint16_t *vnext) __attribute__((always_inline)) {
+        constexpr bool LD = decltype(LOADS)::value != 0;
+        constexpr int NS = NKB * KSTEPS;
+        const int krange = jl + 1 < n ? range : 0, vrange = jl < n ? range : 0;
+        const uint32_t ksoff = (uint32_t)((jl + 1) * kBN) * (uint32_t)(sK * 2);
+        const uint32_t vsoff = (uint32_t)(jl * kBN) * (uint32_t)(sK * 2);
+        u32x4_t ring[RING];
+#pragma unroll
+        for (int i = 0; i < RING; ++i) ring[i] = k_operand(ks, i);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const int t = i / NKB, kb = i % NKB;
+            if (t == 0) mma_s_first_v(sacc[kb], ring[i % RING], qreg[t]);
+            else mma_s_v(sacc[kb], ring[i % RING], qreg[t]);
+            if (i + RING < NS) ring[i % RING] = k_operand(ks, i + RING);
+            if constexpr (LD) {
+                if (i % 2 == 0 && i / 2 < BPL) {
+                    const int b = i / 2;
+                    load_lds16(vbase, vrange, v_voff4[b], vsoff, (lds_void_t *)&vnext[(wl4 * BPL + b) * 512]);
+                    load_lds16(kbase, krange, k_voff4[b], ksoff, (lds_void_t *)&knext[(wl4 * BPL + b) * 512]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
     // Matrix-core step for tile j: O^T += V_{j-1}^T P_{j-1}^T, then
     // S_j^T = K_j Q^T.  No vector-ALU work beyond operand addressing.
     // With LOADS (a compile-time ic<0 or 1>), the tile loads of the phase
@@ -511,8 +578,10 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
         constexpr bool LD = decltype(LOADS)::value != 0;
         if (j >= 1 && visible(j - 1)) {
             const char *vs = (const char *)(vprev + so);
-            if constexpr (D == 256)   // P^T was written by the vector ALU
+            if constexpr (D == 256) {   // P^T was written by the vector ALU
                 asm volatile("s_nop 3" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]));
+                pv_ring(vs);
+            } else {
             if constexpr (MSUM) {
 #pragma unroll
                 for (int u = 0; u < PVSTEPS; ++u) lacc = mfma16_bf16(sum_sel, pb[u], lacc);
@@ -548,8 +617,11 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
             }
 #pragma unroll
             for (int i = 0; i < pf_pv<D>(); ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
         }
-        if (j < n && visible(j)) {
+        if (j < n && visible(j) && D == 256) {
+            s_ring((const char *)(kcur + so), ic<LD>(), jl, knext, vnext);
+        } else if (j < n && visible(j)) {
             if constexpr (LD) { issue_v(jl, vnext); issue_k(jl, knext); }
             const char *ks = (const char *)(kcur + so);
 #pragma unroll
