@@ -116,7 +116,10 @@ __device__ __forceinline__ f32x16_t mfma_bf16(u32x4_t a, u32x4_t b, f32x16_t c)
 // a VALU write of P^T or Q^T read by a product needs 2 wait states (s_nop 3),
 // a product's S^T read by the VALU 11 (s_nop 15), and O^T is read or
 // rewritten by the VALU only after 32.  Accumulating into exactly the
-// previous product's destination needs no gap.
+// previous product's destination needs no gap.  The compiler also takes a
+// product's result as written when it issues, and may copy or move those
+// registers at any later point; so each run of products ends with a
+// statement that waits out the gap and claims its destinations.
 __device__ __forceinline__ void mma_s_first_v(f32x16_t &d, u32x4_t a, u32x4_t bq)
 {
     asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "a"(bq));
@@ -361,7 +364,8 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
         }
         __syncthreads();
         n = tile_count[sg];
-        n_loop = NG == 2 ? max(tile_count[0], tile_count[1]) : n;
+        if constexpr (NG == 2) n_loop = max(tile_count[0], tile_count[NG - 1]);
+        else n_loop = n;
     }
     // absolute key-tile index of the j-th tile of this wavefront's stream
     auto tix = [&](int j) __attribute__((always_inline)) -> int {
@@ -566,6 +570,9 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        // S^T as written (the last products end within 16 wait states): from
+        // here on the compiler may read, copy or move its registers.
+        asm volatile("s_nop 15" : "+v"(sacc[0]), "+v"(sacc[1]));
     };
 
     // Matrix-core step for tile j: O^T += V_{j-1}^T P_{j-1}^T, then
@@ -581,6 +588,11 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
             if constexpr (D == 256) {   // P^T was written by the vector ALU
                 asm volatile("s_nop 3" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]));
                 pv_ring(vs);
+                // O^T as written, before any control-flow merge at which the
+                // compiler may copy it (such a copy can follow the products
+                // at once, e.g. past a barrier the other wavefronts already
+                // wait at).
+                sync_acc();
             } else {
             if constexpr (MSUM) {
 #pragma unroll
@@ -619,29 +631,23 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
             for (int i = 0; i < pf_pv<D>(); ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             }
         }
-        if (j < n && visible(j) && D == 256) {
+        const bool sc = j < n && visible(j);
+        if (sc && D == 256) {
             s_ring((const char *)(kcur + so), ic<LD>(), jl, knext, vnext);
-        } else if (j < n && visible(j)) {
+        } else if (D != 256 && sc) {
             if constexpr (LD) { issue_v(jl, vnext); issue_k(jl, knext); }
             const char *ks = (const char *)(kcur + so);
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                if constexpr (D != 256) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-                }
+                for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
                 const int row = kb * 32 + krow;
                 const char *kr = ks + row * ROW_BYTES;
                 const int sw = k_swz<D>(row);
 #pragma unroll
                 for (int t = 0; t < KSTEPS; ++t) {
                     const u32x4_t a = *(const u32x4_t *)(kr + (((2 * t + hf) ^ sw) * 16));
-                    if constexpr (D == 256) {
-                        if (t == 0) mma_s_first_v(sacc[kb], a, qreg[t]);
-                        else mma_s_v(sacc[kb], a, qreg[t]);
-                    } else {
-                        sacc[kb] = mfma_bf16(a, qreg[t], sacc[kb]);
-                    }
+                    sacc[kb] = mfma_bf16(a, qreg[t], sacc[kb]);
                 }
             }
             // the phase's 2*BPL loads go evenly after the product / operand-read pairs
@@ -731,9 +737,6 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
     bool ref_set = false;      // block-sparse: the wavefront has set its reference (uniform)
     auto softmax_step = [&](int j) __attribute__((always_inline)) {
         if (!visible(j)) return;
-        if constexpr (D == 256) {   // S^T was written by the products
-            asm volatile("s_nop 15" : "+v"(sacc[0]), "+v"(sacc[1]));
-        }
         const int key0 = key_lo + tix(j) * kBN;
         const bool need_mask = (key0 + kBN > Nk) || (CAUSAL && key0 + kBN - 1 > wq0 + off);
         if (need_mask) {
