@@ -9,6 +9,7 @@ import torch
 
 import exact_attention_93_amd as fa
 import oracle
+from tests.fwd_bound import fwd_intervals
 
 # bf16 I/O with fp32 accumulation: max |o - ref| <= 1e-2 and mean <= 1e-3.
 # fp32 I/O: max |o - ref| <= 1e-5.  LSE: |lse - ref| <= 1e-4 * max(1, |ref|).
@@ -30,13 +31,16 @@ def gpu_fwd(q, k, v, causal, scale, num_splits=1):
 
 
 def compare(q, k, v, causal, scale, o, lse, rows=None, kind=None, label="", exact_bounds=False,
-            block_mask=None):
+            block_mask=None, num_splits=None):
     """Compare GPU outputs o [B,N,Hq,d], lse [B,Hq,N] with the oracle on rows.
 
-    exact_bounds=True applies the stated bounds verbatim (the named
-    workloads).  Otherwise (small shapes, where few keys per row leave |O|
-    near 1) the bf16 mean bound also admits the output format's own mean
-    rounding error, ulp(ref)/4, on top of 1e-3.
+    Every element and log-sum-exp must lie in its interval derived from the
+    forward's arithmetic (tests/fwd_bound.py; num_splits as passed to the
+    library, None when unknown, which takes the bound that covers a merge of
+    key ranges).  Besides, exact_bounds=True applies the stated bounds
+    verbatim (the named workloads).  Otherwise (small shapes, where few keys
+    per row leave |O| near 1) the bf16 mean bound also admits the output
+    format's own mean rounding error, ulp(ref)/4, on top of 1e-3.
     """
     kind = kind or ("fp32" if q.dtype == torch.float32 else "bf16")
     if block_mask is None:
@@ -51,6 +55,7 @@ def compare(q, k, v, causal, scale, o, lse, rows=None, kind=None, label="", exac
         r = np.asarray(rows)
         go = o.float().numpy()[r[:, 0], r[:, 2], r[:, 1]].astype(np.float64)
         gl = lse.numpy()[r[:, 0], r[:, 1], r[:, 2]].astype(np.float64)
+    check_intervals(q, k, v, causal, scale, go, gl, rows, kind, label, block_mask, num_splits)
     # rows that see no key: O exactly 0 and lse exactly -inf on both sides
     empty = np.isneginf(rl)
     if empty.any():
@@ -91,6 +96,54 @@ def compare(q, k, v, causal, scale, o, lse, rows=None, kind=None, label="", exac
     assert mean <= tmean, f"mean |dO| {mean} > {tmean}"
     assert lmx <= LSE_REL, f"LSE error {lmx} > {LSE_REL}"
     return mx, mean, lmx
+
+
+def key_ranges(q, k, num_splits):
+    """(merged, keys per range at most) of a forward call with this
+    num_splits: whether it merges several key ranges, and a bound on the
+    length of each (None: unknown, taken as a merge of ranges of any
+    length).  The library cuts the keys into ranges of a multiple of 64,
+    never more ranges than requested, so a range holds at most
+    ceil(ceil(Nk / 64) / nsplit) * 64 keys."""
+    if num_splits is None:
+        return True, None
+    if num_splits == 1:
+        return False, None
+    B, Nq, Hq, d = q.shape
+    Nk = k.shape[1]
+    nsplit = fa.fa_splitkv_num_splits(B, Hq, k.shape[2], Nq, Nk, d, num_splits)
+    if nsplit <= 1:
+        return False, None
+    return True, -(-(-(-Nk // 64)) // nsplit) * 64
+
+
+def check_intervals(q, k, v, causal, scale, go, gl, rows, kind, label, block_mask=None, num_splits=None):
+    """Every output element go [R, d] and log-sum-exp gl [R] (fp64, in the
+    order of rows; None = every row) inside its interval from
+    tests/fwd_bound.py."""
+    B, N, Hq, d = q.shape
+    if rows is None:
+        rows = np.array([(b, h, i) for b in range(B) for h in range(Hq) for i in range(N)], dtype=np.int32)
+    split, range_keys = key_ranges(q, k, num_splits)
+    lo, hi, llo, lhi = fwd_intervals(q, k, v, scale, causal, rows, kind, block_mask=block_mask, split=split,
+                                     range_keys=range_keys)
+    assert np.all(np.isfinite(lo)) and np.all(np.isfinite(hi)) and np.all(lo <= hi), \
+        f"{label}: the derived intervals degenerate (the bound does not hold at this size)"
+    bad = (go < lo) | (go > hi)
+    radius = (hi - lo) / 2
+    say(f"[parity] {label}: derived intervals ({'with' if split else 'without'} a merge) median half-width "
+        f"{np.median(radius):.2e} max {radius.max():.2e}")
+    if bad.any():
+        r, x = np.argwhere(bad)[0]
+        raise AssertionError(f"{label}: {int(bad.sum())} output element(s) outside their derived interval, first "
+                             f"row {tuple(np.asarray(rows)[r])} col {x}: {go[r, x]!r} not in [{lo[r, x]!r}, {hi[r, x]!r}]")
+    fin = np.isfinite(llo)
+    assert np.array_equal(fin, np.isfinite(gl)), f"{label}: rows without keys differ from the derived ones"
+    lbad = (gl[fin] < llo[fin]) | (gl[fin] > lhi[fin])
+    if lbad.any():
+        i = np.nonzero(fin)[0][np.argmax(lbad)]
+        raise AssertionError(f"{label}: {int(lbad.sum())} lse value(s) outside their derived interval, first "
+                             f"row {tuple(np.asarray(rows)[i])}: {gl[i]!r} not in [{llo[i]!r}, {lhi[i]!r}]")
 
 
 def plain_fp32_error(q, k, v, causal, scale, ro, rows, block_mask=None):

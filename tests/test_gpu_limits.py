@@ -60,7 +60,7 @@ def test_longest_prefill_causal_d128():
     torch.cuda.synchronize()
     rows = rows_to_check(1, H, N, seed=901)
     compare(q, k, v, True, 1 / math.sqrt(d), o.cpu(), lse.cpu(), rows=rows, label=f"prefill N={N}",
-            exact_bounds=True)
+            exact_bounds=True, num_splits=1)
 
 
 def test_longest_decode_bf16_d128():
@@ -73,7 +73,8 @@ def test_longest_decode_bf16_d128():
     v = randn((1, Nk, Hkv, d), 912, torch.bfloat16)
     o, lse = fa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=True, num_splits=0)
     torch.cuda.synchronize()
-    compare(q, k, v, True, 1 / math.sqrt(d), o.cpu(), lse.cpu(), label=f"decode Nk={Nk}", exact_bounds=True)
+    compare(q, k, v, True, 1 / math.sqrt(d), o.cpu(), lse.cpu(), label=f"decode Nk={Nk}", exact_bounds=True,
+            num_splits=0)
 
 
 def test_longest_split_fp32_d64():
@@ -85,7 +86,7 @@ def test_longest_split_fp32_d64():
     v = randn((1, Nk, Hkv, d), 922, torch.float32)
     o, lse = fa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=False, num_splits=0)
     torch.cuda.synchronize()
-    compare(q, k, v, False, 1 / math.sqrt(d), o.cpu(), lse.cpu(), label=f"fp32 split Nk={Nk}")
+    compare(q, k, v, False, 1 / math.sqrt(d), o.cpu(), lse.cpu(), label=f"fp32 split Nk={Nk}", num_splits=0)
 
 
 def test_longest_prefill_causal_d256():
@@ -97,7 +98,7 @@ def test_longest_prefill_causal_d256():
     torch.cuda.synchronize()
     rows = rows_to_check(1, H, N, seed=931, extra=4)
     compare(q, k, v, True, 1 / math.sqrt(d), o.cpu(), lse.cpu(), rows=rows, label=f"d256 N={N}",
-            exact_bounds=True)
+            exact_bounds=True, num_splits=1)
 
 
 def test_longest_fp8_causal():
@@ -121,4 +122,4 @@ def test_longest_blocksparse(causal):
     torch.cuda.synchronize()
     rows = rows_to_check(1, Hq, N, seed=952, extra=6)
     compare(q, k, v, causal, 1 / math.sqrt(d), o.cpu(), lse.cpu(), rows=rows, label=f"blocksparse N={N}",
-            block_mask=mask)
+            block_mask=mask, num_splits=1)

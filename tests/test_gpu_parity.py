@@ -23,7 +23,7 @@ def test_small_gqa(N, causal, d, dtype):
     say(f"case small_gqa N={N} causal={causal} d={d} dtype={dtype}")
     q, k, v = rand_inputs(B, N, Hq, Hkv, d, dtype, seed=N * 7 + d + causal)
     o, lse = gpu_fwd(q, k, v, causal, 1 / math.sqrt(d))
-    compare(q, k, v, causal, 1 / math.sqrt(d), o, lse, label=f"N={N}")
+    compare(q, k, v, causal, 1 / math.sqrt(d), o, lse, label=f"N={N}", num_splits=1)
 
 
 @pytest.mark.parametrize("heads", [(1, 1), (4, 1), (3, 3), (6, 2)])
@@ -35,7 +35,7 @@ def test_head_layouts(heads, causal, dtype):
     for B, N, d in [(1, 200, 128), (3, 77, 64)]:
         q, k, v = rand_inputs(B, N, Hq, Hkv, d, dtype, seed=B * 100 + N + Hq)
         o, lse = gpu_fwd(q, k, v, causal, 1 / math.sqrt(d))
-        compare(q, k, v, causal, 1 / math.sqrt(d), o, lse, label=f"B={B} N={N} d={d}")
+        compare(q, k, v, causal, 1 / math.sqrt(d), o, lse, label=f"B={B} N={N} d={d}", num_splits=1)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -45,7 +45,7 @@ def test_scales(scale, dtype):
     q, k, v = rand_inputs(1, 150, 4, 4, 64, dtype, seed=5, q_std=2.0)
     for causal in (False, True):
         o, lse = gpu_fwd(q, k, v, causal, scale)
-        compare(q, k, v, causal, scale, o, lse, label=f"scale={scale} causal={causal}")
+        compare(q, k, v, causal, scale, o, lse, label=f"scale={scale} causal={causal}", num_splits=1)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -55,7 +55,7 @@ def test_peaked_logits_rescale(dtype):
     q, k, v = rand_inputs(1, 700, 2, 1, 128, dtype, seed=9, q_std=8.0)
     for causal in (False, True):
         o, lse = gpu_fwd(q, k, v, causal, 1 / math.sqrt(128))
-        compare(q, k, v, causal, 1 / math.sqrt(128), o, lse, label=f"peaked causal={causal}")
+        compare(q, k, v, causal, 1 / math.sqrt(128), o, lse, label=f"peaked causal={causal}", num_splits=1)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -81,7 +81,7 @@ def test_worked_example(dtype):
         assert abs(round(float(o[0, 0, 0, 0]), 3) - 0.752) < 1e-9
     else:                 # 0.752 is not a bf16 value: within one bf16 ulp (2^-8 at 0.75)
         assert abs(float(o[0, 0, 0, 0]) - 0.752) <= 2 ** -8
-    compare(q, k, v, False, 1 / math.sqrt(2), o, lse, label="worked example")
+    compare(q, k, v, False, 1 / math.sqrt(2), o, lse, label="worked example", num_splits=1)
 
 
 def test_properties_bf16():
@@ -159,4 +159,4 @@ def test_scores_growing_past_the_reference(dtype, causal):
     k[..., 0] = (torch.arange(N, dtype=torch.float32) / 8.0).view(1, N, 1).to(dt)
     for scale in (4.0, 40.0):
         o, lse = gpu_fwd(q, k, v, causal, scale)
-        compare(q, k, v, causal, scale, o, lse, label=f"growing scale={scale}")
+        compare(q, k, v, causal, scale, o, lse, label=f"growing scale={scale}", num_splits=1)

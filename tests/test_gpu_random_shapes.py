@@ -38,7 +38,7 @@ def test_random_configuration(i):
     scale = 1 / math.sqrt(c["d"])
     o, lse = fa.fwd(q.cuda(), k.cuda(), v.cuda(), causal=c["causal"], scale=scale, num_splits=c["splits"])
     torch.cuda.synchronize()
-    compare(q, k, v, c["causal"], scale, o.cpu(), lse.cpu(), label=f"random {i}")
+    compare(q, k, v, c["causal"], scale, o.cpu(), lse.cpu(), label=f"random {i}", num_splits=c["splits"])
 
 
 def draw_bwd(i):

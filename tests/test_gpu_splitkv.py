@@ -43,7 +43,7 @@ def test_split(shape, causal, splits, dtype):
     say(f"case split Nq={Nq} Nk={Nk} causal={causal} splits={splits} (used {used}) dtype={dtype}")
     q, k, v = rand_inputs(2, Nq, 4, 2, d, dtype, seed=Nq + 7 * Nk + splits, Nk=Nk)
     o, lse = gpu_fwd(q, k, v, causal, 1 / math.sqrt(d), num_splits=splits)
-    compare(q, k, v, causal, 1 / math.sqrt(d), o, lse, label=f"Nq={Nq} Nk={Nk} splits={used}")
+    compare(q, k, v, causal, 1 / math.sqrt(d), o, lse, label=f"Nq={Nq} Nk={Nk} splits={used}", num_splits=splits)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
@@ -112,7 +112,8 @@ def test_split_workload(name):
     say(f"case split workload {name} splits={fa.fa_splitkv_num_splits(w.B, w.Hq, w.Hkv, w.N, w.Nkv, w.d, w.splits)}")
     q, k, v = W.gen_inputs(w)
     o, lse = gpu_fwd(q, k, v, w.causal, w.scale, num_splits=w.splits)
-    compare(q, k, v, w.causal, w.scale, o, lse, rows=W.sample_rows(w), label=name, exact_bounds=True)
+    compare(q, k, v, w.causal, w.scale, o, lse, rows=W.sample_rows(w), label=name, exact_bounds=True,
+            num_splits=w.splits)
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -129,7 +130,7 @@ def test_decode_shapes(heads_nq, causal, d, splits):
     say(f"case decode Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal} d={d} splits={splits}")
     q, k, v = rand_inputs(2, Nq, Hq, Hkv, d, "bf16", seed=Hq * 100 + Nq + d + splits, Nk=Nk)
     o, lse = gpu_fwd(q, k, v, causal, 1 / math.sqrt(d), num_splits=splits)
-    compare(q, k, v, causal, 1 / math.sqrt(d), o, lse, label=f"decode Hq={Hq} Hkv={Hkv} Nq={Nq}")
+    compare(q, k, v, causal, 1 / math.sqrt(d), o, lse, label=f"decode Hq={Hq} Hkv={Hkv} Nq={Nq}", num_splits=splits)
 
 
 def test_decode_rows_without_keys():
@@ -138,5 +139,5 @@ def test_decode_rows_without_keys():
     q, k, v = rand_inputs(1, 12, 4, 1, 128, "bf16", seed=5, Nk=7)
     for splits in (1, 2):
         o, lse = gpu_fwd(q, k, v, True, 0.1, num_splits=splits)
-        compare(q, k, v, True, 0.1, o, lse, label=f"decode empty rows splits={splits}")
+        compare(q, k, v, True, 0.1, o, lse, label=f"decode empty rows splits={splits}", num_splits=splits)
         assert torch.all(o[0, :5].float() == 0) and torch.all(torch.isneginf(lse[0, :, :5]))

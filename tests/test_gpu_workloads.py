@@ -23,7 +23,7 @@ def test_workload(name):
     torch.cuda.synchronize()
     o, lse = o.cpu(), lse.cpu()
     rows = None if w.dtype == "fp32" else W.sample_rows(w)
-    compare(q, k, v, w.causal, w.scale, o, lse, rows=rows, label=name, exact_bounds=True)
+    compare(q, k, v, w.causal, w.scale, o, lse, rows=rows, label=name, exact_bounds=True, num_splits=1)
 
 
 @pytest.mark.parametrize("name", list(W.FP32_WORKLOADS))
@@ -34,4 +34,5 @@ def test_fp32_workload(name):
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     o, lse = fa.fwd(qd, kd, vd, causal=w.causal, scale=w.scale, num_splits=w.splits)
     torch.cuda.synchronize()
-    compare(q, k, v, w.causal, w.scale, o.cpu(), lse.cpu(), rows=W.sample_rows(w), label=name, exact_bounds=True)
+    compare(q, k, v, w.causal, w.scale, o.cpu(), lse.cpu(), rows=W.sample_rows(w), label=name, exact_bounds=True,
+            num_splits=w.splits)
