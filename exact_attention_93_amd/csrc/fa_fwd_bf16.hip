@@ -704,7 +704,9 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
         return max_halves(mx);
     };
     // P = 2^(s*c - m) rounded to bf16 and packed as the next product's B
-    // operand; returns the fp32 row sum of the unrounded values.
+    // operand; returns the fp32 row sum of the unrounded values.  The sums
+    // start from the first pair (adding +0 first would cost an instruction:
+    // it is not folded, for the sake of -0, which exp2 never returns).
     auto exps = [&]() __attribute__((always_inline)) -> float {
         const float m_sub = m_run == -INFINITY ? 0.f : m_run;
         float rf0 = 0.f, rf1 = 0.f;
@@ -715,8 +717,8 @@ __global__ void __launch_bounds__(wg_threads<D>(), 1) fwd_bf16_kernel(FwdParams 
             for (int w = 0; w < 4; ++w) {
                 const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][base + 2 * w], c, -m_sub));
                 const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][base + 2 * w + 1], c, -m_sub));
-                rf0 += e0;
-                rf1 += e1;
+                rf0 = (u == 0 && w == 0) ? e0 : rf0 + e0;
+                rf1 = (u == 0 && w == 0) ? e1 : rf1 + e1;
                 pb[u][w] = pack_bf16(e0, e1);
             }
         }

@@ -89,11 +89,14 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
-// Four floats -> four e4m3 codes (round to nearest even) in one dword.
+// Four floats -> four e4m3 codes (round to nearest even) in one dword: c, d
+// into the high half, then a, b into the low half.  The first conversion
+// keeps the other half of the dword it is given; giving it c's own bits
+// (c is dead after it) spares a register cleared for the purpose.
 __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d)
 {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, __builtin_bit_cast(int, c), true);
+    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, w, false);
 }
 
 __device__ __forceinline__ float max_halves(float x)
@@ -344,8 +347,8 @@ __global__ void __launch_bounds__(kThreads, 1) fwd_fp8_kernel(FwdParams p)
             float e[4];
 #pragma unroll
             for (int z = 0; z < 4; ++z) e[z] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i0 + z], c, -m_sub));
-            rf0 += e[0] + e[2];
-            rf1 += e[1] + e[3];
+            rf0 = w == 0 ? e[0] + e[2] : rf0 + (e[0] + e[2]);   // from the first pair, not from +0
+            rf1 = w == 0 ? e[1] + e[3] : rf1 + (e[1] + e[3]);
             pb[w] = pack_fp8x4(e[0], e[1], e[2], e[3]);
         }
         l_run = l_run * alpha + (rf0 + rf1);
