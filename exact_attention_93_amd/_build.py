@@ -22,7 +22,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libfa.so")
 SINGLE_STAGE_LIB_PATH = os.path.join(PKG, "libfa_single_stage.so")
-SINGLE_STAGE_SOURCES = ("fa_fwd_bf16.hip", "fa_fwd_fp8.hip", "fa_bwd_bf16.hip")   # read FA_SINGLE_STAGE
+SINGLE_STAGE_SOURCES = ("fa_fwd_bf16.hip", "fa_fwd_fp8.hip", "fa_fwd_f32.hip", "fa_bwd_bf16.hip")   # read FA_SINGLE_STAGE
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are switched off for all device code.

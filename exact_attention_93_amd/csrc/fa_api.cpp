@@ -417,7 +417,7 @@ int fa_version(void) { return kVersion; }
 int fa_lds_stages(void)
 {
     const int n = fa::fwd_bf16_lds_stages();
-    return (n == fa::fwd_fp8_lds_stages() && n == fa::bwd_lds_stages()) ? n : 0;
+    return (n == fa::fwd_fp8_lds_stages() && n == fa::fwd_f32_lds_stages() && n == fa::bwd_lds_stages()) ? n : 0;
 }
 
 }  // extern "C"

@@ -3,9 +3,12 @@
 //
 // Same algorithm and work partition as the bf16 kernel (Q-block-outer loop,
 // online-softmax merge with deferred normalisation, causal tiles above the
-// diagonal skipped; see fa_fwd_bf16.hip for the citations), written for
-// accuracy rather than peak speed: 32-key tiles, one LDS buffer, V kept in
-// its natural [key][d] layout.
+// diagonal skipped; see fa_fwd_bf16.hip for the citations), with 32-key
+// tiles and V kept in its natural [key][d] layout.  Two LDS buffers: the
+// next tile's loads go to registers while the current tile's products run,
+// and into the other buffer after them, one barrier per tile.  The
+// single-stage build (FA_SINGLE_STAGE) loads each tile into one buffer
+// between two barriers instead; the arithmetic is the same.
 //
 // Layout (32x32x2 fp32 MFMA): A lane l supplies A[l % 32][l / 32], B lane l
 // supplies B[l / 32][l % 32]; the 32x32 accumulator holds column l % 32 in
@@ -41,8 +44,9 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(FwdParams p)
     constexpr int XB = D / 32;
     constexpr int LOADS = kBN * D / 4 / kThreads;   // float4 loads per thread per tensor
 
-    __shared__ __attribute__((aligned(16))) float Ks[kBN * KP];
-    __shared__ __attribute__((aligned(16))) float Vs[kBN * D];
+    constexpr int NBUF = kSingleStage ? 1 : 2;
+    __shared__ __attribute__((aligned(16))) float Ks[NBUF][kBN * KP];
+    __shared__ __attribute__((aligned(16))) float Vs[NBUF][kBN * D];
 
     int b, h, tile, split;
     decode_tile(p, b, h, tile, split);
@@ -80,31 +84,44 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(FwdParams p)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[xb][i] = 0.f;
 
-    for (int j = kt_lo; j < kt_hi; ++j) {
-        const int key0 = j * kBN;
-        __syncthreads();   // previous tile fully consumed
+    // Tile j of K and V: global memory -> registers (fetch), registers ->
+    // LDS buffer (store); keys at or past Nk read as zero.
+    f32x4_t kreg[LOADS], vreg[LOADS];
+    auto fetch = [&](int j) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < LOADS; ++r) {
             const int idx = tid + r * kThreads;          // float4 index within the tile
             const int row = idx / (D / 4), col = (idx % (D / 4)) * 4;
-            const int key = key0 + row;
-            f32x4_t kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
+            const int key = j * kBN + row;
+            kreg[r] = vreg[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             if (key < Nk) {
-                kv = *(const f32x4_t *)(kbase + key * sK + col);
-                vv = *(const f32x4_t *)(vbase + key * sK + col);
+                kreg[r] = *(const f32x4_t *)(kbase + key * sK + col);
+                vreg[r] = *(const f32x4_t *)(vbase + key * sK + col);
             }
-            *(f32x4_t *)&Ks[row * KP + col] = kv;
-            *(f32x4_t *)&Vs[row * D + col] = vv;
         }
-        __syncthreads();
-        if (wq0 >= Nq || (CAUSAL && key0 > wq0 + 31 + off)) continue;   // no row of this wave sees the tile
+    };
+    auto store = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < LOADS; ++r) {
+            const int idx = tid + r * kThreads;
+            const int row = idx / (D / 4), col = (idx % (D / 4)) * 4;
+            *(f32x4_t *)&Ks[buf][row * KP + col] = kreg[r];
+            *(f32x4_t *)&Vs[buf][row * D + col] = vreg[r];
+        }
+    };
+    // The products and the softmax of tile j from LDS buffer buf.
+    auto tile_step = [&](int j, int buf) __attribute__((always_inline)) {
+        const int key0 = j * kBN;
+        if (wq0 >= Nq || (CAUSAL && key0 > wq0 + 31 + off)) return;   // no row of this wave sees the tile
+        const float *ks = Ks[buf];
+        const float *vs = Vs[buf];
 
         f32x16_t sacc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
 #pragma unroll
         for (int s = 0; s < S4; ++s) {
-            const f32x4_t a = *(const f32x4_t *)&Ks[lq * KP + 8 * s + 4 * hf];
+            const f32x4_t a = *(const f32x4_t *)&ks[lq * KP + 8 * s + 4 * hf];
 #pragma unroll
             for (int e = 0; e < 4; ++e) sacc = mfma_f32(a[e], qreg[s][e], sacc);
         }
@@ -128,7 +145,7 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(FwdParams p)
         for (int i = 0; i < 16; ++i) {
             const float e = exp2f(__builtin_fmaf(sacc[i], c, -m_sub));
             sacc[i] = e;
-            rs += e;
+            rs = i == 0 ? e : rs + e;   // from the first value, not from +0
         }
         l_run = l_run * alpha + rs;
 #pragma unroll
@@ -138,8 +155,34 @@ __global__ void __launch_bounds__(kThreads) fwd_f32_kernel(FwdParams p)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int key = 8 * (i >> 2) + 4 * hf + (i & 3);
-                oacc[xb] = mfma_f32(Vs[key * D + xb * 32 + lq], sacc[i], oacc[xb]);
+                oacc[xb] = mfma_f32(vs[key * D + xb * 32 + lq], sacc[i], oacc[xb]);
             }
+        }
+    };
+
+    if constexpr (kSingleStage) {
+        for (int j = kt_lo; j < kt_hi; ++j) {
+            __syncthreads();   // previous tile fully consumed
+            fetch(j);
+            store(0);
+            __syncthreads();
+            tile_step(j, 0);
+        }
+    } else {
+        if (kt_lo < kt_hi) {
+            fetch(kt_lo);
+            store(0);
+        }
+        __syncthreads();
+        for (int j = kt_lo; j < kt_hi; ++j) {
+            // Buffer buf holds tile j; the other was last read for tile j-1,
+            // and the barrier that ended that tile ended those reads.
+            const int buf = (j - kt_lo) & 1;
+            const bool more = j + 1 < kt_hi;
+            if (more) fetch(j + 1);
+            tile_step(j, buf);
+            if (more) store(buf ^ 1);
+            __syncthreads();
         }
     }
 
@@ -183,6 +226,8 @@ hipError_t launch_d(const FwdParams &p, hipStream_t stream)
 }
 
 }  // namespace
+
+int fwd_f32_lds_stages() { return kSingleStage ? 1 : 2; }
 
 hipError_t launch_fwd_f32(const FwdParams &p_in, int d, hipStream_t stream)
 {

@@ -56,6 +56,7 @@ constexpr bool kSingleStage = FA_SINGLE_STAGE != 0;
 // the stage count each kernel source was built with (1 or 2)
 int fwd_bf16_lds_stages();
 int fwd_fp8_lds_stages();
+int fwd_f32_lds_stages();
 int bwd_lds_stages();
 
 hipError_t launch_fwd_bf16(const FwdParams &p, int d, hipStream_t stream);

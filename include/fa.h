@@ -301,8 +301,8 @@ int fa_version(void);
  * after every read of the one stage has ended; 0 if the kernel sources were
  * built inconsistently.  The debug build exists to check the normal build's
  * wait and barrier placement: its outputs must be equal bit for bit.  Covers
- * the bf16 and fp8 forward kernels and the backward; the fp32 forward and
- * the decoding kernel keep one stage in both builds.  No error case. */
+ * the bf16, fp8 and fp32 forward kernels and the backward; the decoding
+ * kernel keeps one stage in both builds.  No error case. */
 int fa_lds_stages(void);
 
 #ifdef __cplusplus

@@ -6,8 +6,8 @@ must give the same outputs bit for bit; a missing wait or barrier in its
 schedule (a read of a stage still being filled, or a load into a stage still
 being read) shows up as a difference.  Covers every entry point that runs
 these kernels: the bf16 forward (whole-sequence, split key ranges, block
-mask; d = 64, 128, 256), the fp8 forward in both scale forms, and the
-backward."""
+mask; d = 64, 128, 256), the fp32 forward (whole-sequence and split), the
+fp8 forward in both scale forms, and the backward."""
 import contextlib
 
 import pytest
@@ -95,6 +95,30 @@ def test_split_key_ranges(libs, shape, causal, splits):
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     assert_bitwise(run_both(libs, lambda: fa.fwd(qd, kd, vd, causal=causal, num_splits=splits)),
                    f"split {shape} splits={splits}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 1), (300, 300), (1000, 1000), (129, 1000), (1000, 129)],
+                         ids=lambda s: f"q{s[0]}k{s[1]}")
+def test_fp32(libs, shape, causal, d):
+    Nq, Nk = shape
+    say(f"case single-stage fp32 Nq={Nq} Nk={Nk} causal={causal} d={d}")
+    q, k, v = rand_inputs(2, Nq, 4, 2, d, "fp32", seed=4400 + Nq + Nk + d, Nk=Nk)
+    qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
+    assert_bitwise(run_both(libs, lambda: fa.fwd(qd, kd, vd, causal=causal)), f"fp32 {shape} d={d}")
+    if Nk >= 256:
+        assert_bitwise(run_both(libs, lambda: fa.fwd(qd, kd, vd, causal=causal, num_splits=3)),
+                       f"fp32 split {shape} d={d}")
+
+
+@pytest.mark.parametrize("name", list(W.FP32_WORKLOADS))
+def test_fp32_workloads(libs, name):
+    w = W.FP32_WORKLOADS[name]
+    say(f"case single-stage workload {name}")
+    q, k, v = (t.cuda() for t in W.gen_inputs(w))
+    assert_bitwise(run_both(libs, lambda: fa.fwd(q, k, v, causal=w.causal, scale=w.scale, num_splits=w.splits)),
+                   name)
 
 
 @pytest.mark.parametrize("d", [64, 128, 256])
