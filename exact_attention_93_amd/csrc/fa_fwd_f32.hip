@@ -36,8 +36,11 @@ __device__ __forceinline__ f32x16_t mfma_f32(float a, float b, f32x16_t c)
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// Two wavefronts per SIMD (two workgroups per compute unit, 66.5 KB of LDS
+// each): the register budget is 256 per wavefront, which the kernel meets
+// without spilling (at d = 128, 249 VGPRs and the accumulators among them).
 template <int D, bool CAUSAL, bool SPLIT>
-__global__ void __launch_bounds__(kThreads) fwd_f32_kernel(FwdParams p)
+__global__ void __launch_bounds__(kThreads, 2) fwd_f32_kernel(FwdParams p)
 {
     constexpr int KP = D + 4;              // K row pitch (floats)
     constexpr int S4 = D / 8;              // float4 groups of Q per lane
